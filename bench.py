@@ -1,0 +1,209 @@
+"""Throughput of forward convolution (implicit im2col + MFMA GEMM) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole workload (every conv layer, with its bias
+and GELU epilogue) over one batch of seeded synthetic input already resident
+in HBM.  Default workload: the Whisper-tiny conv frontend at batch 1 in fp32
+(conv1d 80->384 k3 s1 p1 + bias + GELU, then 384->384 k3 s2 p1 + bias +
+GELU on a [1, 80, 3000] input).  Other workloads (--workload):
+conv1d_80to384_f32_b1, whisper_frontend_bf16_b32, grouped_conv2d_bf16,
+grouped_conv3d_bf16_dil2.
+
+Prints ONE JSON line.  value = useful TFLOP/s of the whole step (2*MACs
+counting padded taps, over the wall time of K steps bracketed by device
+synchronisation).  roofline = the dominant (most flop) kernel: its useful
+flop per launch over its mean launch time, taken from HIP events recorded
+around each of its launches on the stream it runs on, against the MI355X
+dense MFMA peak of its dtype.  cpu_baseline = the fp64 oracle on the host
+cores over a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
+HBM_GBS = 8000.0
+METRIC = "conv fwd useful TFLOP/s and % of MFMA peak (Whisper frontend, grouped bf16)"
+DEFAULT_WORKLOAD = "whisper_frontend_f32_b1"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in ("convolution_forward_implicit_amd/csrc/igemm_kernel.h",
+                "convolution_forward_implicit_amd/csrc/conv_fwd.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, layer_index, launches_bytes):
+    """HBM bytes per launch of the dominant kernel, from the committed
+    counter summary (profiles/traffic_<workload>.json), or None when there
+    is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("layer") != layer_index:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(W, target_s):
+    """Times the fp64 oracle on the host cores over a bounded sample of the
+    workload: whole layers when a layer is small, otherwise a random sample
+    of its outputs; the rate is useful flop of the sample over its time."""
+    import numpy as np
+    from oracle import ref
+    flop, secs, parts = 0.0, 0.0, []
+    budget = target_s / len(W["layers"])
+    x = W["x"]
+    for li, (p, hb, ge) in enumerate(W["layers"]):
+        w, b = W["w"][li], W["b"][li]
+        _, _, _, ys = ref.shapes(p)
+        xin = np.ascontiguousarray(x, dtype=np.float64) if x is not None else None
+        if xin is None:
+            xin = np.zeros(ref.shapes(p)[0])
+        per_out = ref.useful_flop(p) / float(np.prod(ys))
+        # calibrate on a small sample, then size the timed sample to the budget
+        rng = np.random.Generator(np.random.PCG64(li))
+        idx = rng.integers(0, int(np.prod(ys)), 2000)
+        t0 = time.perf_counter()
+        ref.conv_fwd_points(p, xin, w, b, ge, idx)
+        t_cal = max(time.perf_counter() - t0, 1e-4)
+        n = int(min(np.prod(ys), max(2000, 2000 * budget / t_cal)))
+        if n >= np.prod(ys):
+            t0 = time.perf_counter()
+            y = ref.conv_fwd(p, xin, w, b, ge, want_absdot=False)
+            dt = time.perf_counter() - t0
+            parts.append("layer %d: all %d outputs" % (li + 1, int(np.prod(ys))))
+            flop += ref.useful_flop(p)
+            x = y
+        else:
+            idx = rng.integers(0, int(np.prod(ys)), n)
+            t0 = time.perf_counter()
+            ref.conv_fwd_points(p, xin, w, b, ge, idx)
+            dt = time.perf_counter() - t0
+            parts.append("layer %d: %d random outputs of %d" % (li + 1, n, int(np.prod(ys))))
+            flop += per_out * n
+            x = None
+        secs += dt
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": ref.max_threads(),
+            "kind": "oracle", "sample": "; ".join(parts) + " (fp64 direct loops, %.1f s)" % secs}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); a %d-GPU run is not "
+              "supported -- the path needs no collective and would shard by batch" % max(args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthdata as sd
+    from convolution_forward_implicit_amd import ConvFwd
+
+    W = sd.workload(args.workload)
+    dt = W["dtype"]
+    dev = torch.device("cuda:0")
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(tdt).contiguous()
+
+    convs, ws, bs, outs = [], [], [], []
+    x0 = up(W["x"])
+    for li, (p, hb, ge) in enumerate(W["layers"]):
+        c = ConvFwd(p, dt, hb, ge)
+        convs.append(c)
+        ws.append(up(W["w"][li]))
+        bs.append(up(W["b"][li]) if hb else None)
+        outs.append(torch.empty(c.y_shape, dtype=tdt, device=dev))
+    flops = [c.useful_flop() for c in convs]
+    dom = int(np.argmax(flops))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None, i=0):
+        x = x0
+        for li, c in enumerate(convs):
+            if ev is not None and li == dom:
+                ev[0][i].record(stream)
+            c(x, ws[li], bs[li], out=outs[li], stream=stream)
+            if ev is not None and li == dom:
+                ev[1][i].record(stream)
+            x = outs[li]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
+          [torch.cuda.Event(enable_timing=True) for _ in range(K)])
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(ev, i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(*ev)]))
+
+    total_flop = float(sum(flops))
+    value = total_flop / (ms_step * 1e-3) / 1e12
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
+    esz = 4 if dt == "f32" else 2
+    alg_bytes = esz * (int(np.prod(convs[dom].x_shape)) + int(np.prod(convs[dom].w_shape)) +
+                       (int(np.prod(convs[dom].b_shape)) if convs[dom].has_bias else 0) +
+                       int(np.prod(convs[dom].y_shape)))
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dt],
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4),
+            "traffic": recorded_traffic(args.workload, dom, alg_bytes),
+            "kernel": "layer %d: %s" % (dom + 1, convs[dom].describe()),
+            "kernel_ms": round(dom_ms, 5), "algorithmic_bytes": alg_bytes,
+            "hbm_GBs_algorithmic": round(alg_bytes / (dom_ms * 1e-3) / 1e9, 1)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(W, args.cpu_seconds)
+        cpu["value"] = round(cpu["value"], 6)
+
+    line = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": W["layers"][0][0]["N"],
+                   "layers": [c.describe() for c in convs], "useful_gflop_per_step": round(total_flop / 1e9, 4),
+                   "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

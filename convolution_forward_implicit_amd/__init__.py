@@ -1,0 +1,108 @@
+"""convfwd: forward convolution as implicit im2col + tiled MFMA GEMM on MI355X.
+
+The computation lives in the HIP library libconvfwd.so (C ABI in
+include/convfwd.h); this package only marshals arguments.  PyTorch supplies
+device memory and streams:
+
+    from convolution_forward_implicit_amd import ConvFwd
+    conv = ConvFwd(problem, "bf16", has_bias=True, gelu=True)
+    y = conv(x, w, bias)          # x, w, bias: contiguous cuda tensors in the
+                                  # library layouts (NDHWGC, GKZYXC, GK)
+
+A problem is a dict {"N", "G", "C", "K", "in": (D, H, W), "filt": (Z, Y, X),
+"stride", "pad", "dil"} (C and K per group); a 1-D convolution has
+D = H = 1, a 2-D one D = 1.
+"""
+from . import capi
+from .capi import ConvError  # noqa: F401
+
+__all__ = ["ConvFwd", "ConvError", "capi", "desc_from_problem"]
+
+
+def _ndim(p):
+    triv = lambda i: (p["in"][i] == 1 and p["filt"][i] == 1 and p["stride"][i] == 1
+                      and p["pad"][i] == 0 and p["dil"][i] == 1)
+    if not triv(0):
+        return 3
+    return 2 if not triv(1) else 1
+
+
+def desc_from_problem(p, dtype, has_bias=False, gelu=False):
+    return capi.make_desc(_ndim(p), dtype, p["N"], p["G"], p["C"], p["K"], p["in"], p["filt"],
+                          p["stride"], p["pad"], p["dil"], has_bias, gelu)
+
+
+class ConvFwd:
+    """A plan for one problem.  Calling it enqueues the kernel on the current
+    torch stream (or `stream`) and returns y."""
+
+    def __init__(self, problem, dtype, has_bias=False, gelu=False, config=None):
+        self.problem = dict(problem)
+        self.dtype = dtype
+        self.has_bias = bool(has_bias)
+        self.gelu = bool(gelu)
+        self._desc = desc_from_problem(problem, dtype, has_bias, gelu)
+        self._plan = (capi.conv_fwd_create(self._desc) if config is None
+                      else capi.conv_fwd_create_with_config(self._desc, config))
+        self.out_dims = capi.conv_fwd_out_dims(self._plan)
+        p = self.problem
+        self.x_shape = (p["N"],) + tuple(p["in"]) + (p["G"], p["C"])
+        self.w_shape = (p["G"], p["K"]) + tuple(p["filt"]) + (p["C"],)
+        self.b_shape = (p["G"], p["K"])
+        self.y_shape = (p["N"],) + self.out_dims + (p["G"], p["K"])
+
+    def useful_flop(self):
+        """2 * multiply-adds counting padded taps (the conv1d issue's way of
+        turning dispatch times into useful throughput)."""
+        p = self.problem
+        n = 2 * p["N"] * p["G"] * p["K"] * p["C"]
+        for v in self.out_dims + tuple(p["filt"]):
+            n *= v
+        return n
+
+    def describe(self):
+        return capi.conv_fwd_describe(self._plan)
+
+    def close(self):
+        if getattr(self, "_plan", None):
+            capi.conv_fwd_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _tensor(self, t, shape, name, torch):
+        tdt = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a cuda tensor" % name)
+        if t.dtype != tdt:
+            raise ValueError("%s must be %s, got %s" % (name, tdt, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        n = 1
+        for s in shape:
+            n *= s
+        if t.numel() != n:
+            raise ValueError("%s has %d elements, expected shape %r" % (name, t.numel(), shape))
+        return t.data_ptr()
+
+    def __call__(self, x, w, bias=None, out=None, stream=None):
+        import torch
+        xp = self._tensor(x, self.x_shape, "x", torch)
+        wp = self._tensor(w, self.w_shape, "w", torch)
+        bp = None
+        if self.has_bias:
+            if bias is None:
+                raise ValueError("this plan has a bias")
+            bp = self._tensor(bias, self.b_shape, "bias", torch)
+        elif bias is not None:
+            raise ValueError("this plan has no bias")
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
+        yp = self._tensor(out, self.y_shape, "out", torch)
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        capi.conv_fwd_run(self._plan, xp, wp, bp, yp, s.cuda_stream)
+        return out

@@ -1,0 +1,149 @@
+"""ctypes binding of the C ABI in include/convfwd.h -- argument marshalling
+only; every step of the computation runs in the HIP library.
+
+The functions keep the C names.  Pointers are plain integers (device
+addresses) and the stream is a hipStream_t handle as an integer (0 = null
+stream).  Errors come back as ConvError carrying the status and the
+library's message.  Loading fails loudly if libconvfwd.so has not been built.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconvfwd.so")
+
+CONV_DT_F32 = 0
+CONV_DT_BF16 = 1
+DTYPES = {"f32": CONV_DT_F32, "bf16": CONV_DT_BF16}
+
+CONV_OK = 0
+CONV_ERR_INVALID_ARG = 1
+CONV_ERR_UNSUPPORTED = 2
+CONV_ERR_HIP = 3
+CONV_ERR_NOMEM = 4
+STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED",
+                3: "CONV_ERR_HIP", 4: "CONV_ERR_NOMEM"}
+
+EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims",
+            "conv_fwd_run", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
+            "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error"]
+
+
+class conv_fwd_desc_t(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("N", ctypes.c_int64), ("G", ctypes.c_int64),
+                ("C", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("in_", ctypes.c_int64 * 3), ("filt", ctypes.c_int64 * 3),
+                ("stride", ctypes.c_int64 * 3), ("pad", ctypes.c_int64 * 3),
+                ("dilation", ctypes.c_int64 * 3),
+                ("has_bias", ctypes.c_int32), ("gelu", ctypes.c_int32)]
+
+
+class ConvError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("convfwd HIP library not built: %s is missing "
+                              "(run python -m convolution_forward_implicit_amd.build)" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        D = ctypes.POINTER(conv_fwd_desc_t)
+        L.conv_fwd_create.argtypes = [D, ctypes.POINTER(P)]
+        L.conv_fwd_create.restype = ctypes.c_int
+        L.conv_fwd_create_with_config.argtypes = [D, ctypes.c_int32, ctypes.POINTER(P)]
+        L.conv_fwd_create_with_config.restype = ctypes.c_int
+        L.conv_fwd_out_dims.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_fwd_out_dims.restype = ctypes.c_int
+        L.conv_fwd_run.argtypes = [P, P, P, P, P, P]
+        L.conv_fwd_run.restype = ctypes.c_int
+        L.conv_fwd_destroy.argtypes = [P]
+        L.conv_fwd_destroy.restype = None
+        L.conv_fwd_describe.argtypes = [P]
+        L.conv_fwd_describe.restype = ctypes.c_char_p
+        L.conv_fwd_num_configs.argtypes = []
+        L.conv_fwd_num_configs.restype = ctypes.c_int32
+        L.conv_fwd_config_name.argtypes = [ctypes.c_int32]
+        L.conv_fwd_config_name.restype = ctypes.c_char_p
+        L.conv_fwd_config_dtype.argtypes = [ctypes.c_int32]
+        L.conv_fwd_config_dtype.restype = ctypes.c_int32
+        L.conv_fwd_last_error.argtypes = []
+        L.conv_fwd_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st):
+    if st != CONV_OK:
+        raise ConvError(st, lib().conv_fwd_last_error().decode())
+
+
+def make_desc(ndim, dtype, N, G, C, K, inp, filt, stride=(1, 1, 1), pad=(0, 0, 0),
+              dilation=(1, 1, 1), has_bias=False, gelu=False):
+    """A conv_fwd_desc_t; spatial tuples are (D, H, W) order, length 3."""
+    d = conv_fwd_desc_t()
+    d.ndim = int(ndim)
+    d.dtype = DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+    d.N, d.G, d.C, d.K = int(N), int(G), int(C), int(K)
+    for i in range(3):
+        d.in_[i], d.filt[i] = int(inp[i]), int(filt[i])
+        d.stride[i], d.pad[i], d.dilation[i] = int(stride[i]), int(pad[i]), int(dilation[i])
+    d.has_bias, d.gelu = int(bool(has_bias)), int(bool(gelu))
+    return d
+
+
+def conv_fwd_create(desc):
+    plan = ctypes.c_void_p()
+    _check(lib().conv_fwd_create(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan.value
+
+
+def conv_fwd_create_with_config(desc, config):
+    plan = ctypes.c_void_p()
+    _check(lib().conv_fwd_create_with_config(ctypes.byref(desc), int(config), ctypes.byref(plan)))
+    return plan.value
+
+
+def conv_fwd_out_dims(plan):
+    out = (ctypes.c_int64 * 3)()
+    _check(lib().conv_fwd_out_dims(plan, out))
+    return tuple(int(v) for v in out)
+
+
+def conv_fwd_run(plan, x, w, bias, y, stream=0):
+    _check(lib().conv_fwd_run(plan, x, w, bias, y, stream))
+
+
+def conv_fwd_destroy(plan):
+    lib().conv_fwd_destroy(plan)
+
+
+def conv_fwd_describe(plan):
+    return lib().conv_fwd_describe(plan).decode()
+
+
+def conv_fwd_num_configs():
+    return int(lib().conv_fwd_num_configs())
+
+
+def conv_fwd_config_name(config):
+    r = lib().conv_fwd_config_name(int(config))
+    return None if r is None else r.decode()
+
+
+def conv_fwd_config_dtype(config):
+    return int(lib().conv_fwd_config_dtype(int(config)))
+
+
+def conv_fwd_last_error():
+    return lib().conv_fwd_last_error().decode()

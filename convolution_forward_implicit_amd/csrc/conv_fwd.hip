@@ -1,0 +1,346 @@
+// Host side of the C ABI declared in include/convfwd.h: descriptor
+// validation and canonicalisation to a 3-D problem, output extents, the
+// per-shape tile-configuration selector and the launcher.
+//
+// Canonicalisation follows the ExecuTorch conv1d issue ("Suggested fix": a
+// conv1d is a conv2d with a singleton height) one step further: every
+// problem becomes a 3-D one with unit leading dims, so one kernel template
+// serves 1-D, 2-D and 3-D.  The selector is the analytic counterpart of the
+// per-problem kernel choice in the Composable Kernel grouped-conv note
+// (section 1: choosing among tile/pipeline variants per dim tuple), and like
+// the onnxruntime subgroup-matrix MatMul change it prefers big tiles for big
+// problems and smaller ones where big tiles would leave compute units idle.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/convfwd.h"
+#include "igemm_kernel.h"
+
+namespace convfwd {
+namespace {
+
+thread_local char g_err[512] = "";
+
+conv_status_t fail(conv_status_t st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+typedef void (*launch_fn)(const KParams &, int grid, hipStream_t);
+
+template <int DT, int BM, int BN, int BK, int WM, int WN, int VEC>
+void launch(const KParams &kp, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((igemm_fwd_kernel<DT, BM, BN, BK, WM, WN, VEC>), dim3(grid),
+                       dim3(WM * WN * 64), 0, s, kp);
+}
+
+struct TileCfg {
+    int dtype;          // conv_dtype_t
+    int BM, BN, BK, WM, WN, VEC;
+    int lds_bytes;
+    launch_fn fn;
+    const char *name;
+};
+
+#define CFG(DT, BM, BN, BK, WM, WN, VEC)                                                 \
+    TileCfg{DT, BM, BN, BK, WM, WN, VEC,                                                 \
+            IgemmShape<DT, BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                          \
+            &launch<DT, BM, BN, BK, WM, WN, VEC>,                                        \
+            (DT ? "bf16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC                 \
+                : "f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC)}
+
+// One candidate table, shared by the selector, forced-config creation and
+// the sweeps.  VEC = 16 bytes of channels per load; the VEC = 1 entries serve
+// channel counts that are not a multiple of the vector.
+const TileCfg kCfgs[] = {
+    CFG(1, 128, 128, 64, 2, 2, 8),
+    CFG(1, 128, 64, 64, 2, 2, 8),
+    CFG(1, 128, 32, 64, 4, 1, 8),
+    CFG(1, 64, 64, 64, 2, 2, 8),
+    CFG(1, 64, 32, 64, 2, 2, 8),
+    CFG(1, 256, 64, 64, 4, 1, 8),
+    CFG(1, 64, 64, 32, 2, 2, 1),
+    CFG(0, 64, 64, 32, 2, 2, 4),
+    CFG(0, 32, 64, 32, 1, 4, 4),
+    CFG(0, 64, 32, 32, 4, 1, 4),
+    CFG(0, 32, 32, 32, 2, 2, 4),
+    CFG(0, 128, 64, 32, 2, 2, 4),
+    CFG(0, 64, 64, 16, 2, 2, 1),
+};
+constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
+
+int device_cu_count()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) { (void)hipGetLastError(); return 256; }
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus > 0 ? cus : 256;
+}
+
+}  // namespace
+}  // namespace convfwd
+
+using namespace convfwd;
+
+struct conv_fwd_plan {
+    conv_fwd_desc_t desc;
+    int64_t out[3];
+    int64_t x_elems, w_elems, b_elems, y_elems;
+    int esz;
+    int cfg;
+    int grid;
+    KParams kp;      // pointers filled per run
+    char text[256];
+};
+
+namespace {
+
+int64_t extent(int64_t I, int64_t F, int64_t s, int64_t p, int64_t d)
+{
+    int64_t span = I + 2 * p - d * (F - 1) - 1;
+    return span < 0 ? 0 : span / s + 1;
+}
+
+conv_status_t validate(const conv_fwd_desc_t *d, int64_t out[3])
+{
+    if (!d) return fail(CONV_ERR_INVALID_ARG, "descriptor is NULL");
+    if (d->ndim < 1 || d->ndim > 3) return fail(CONV_ERR_INVALID_ARG, "ndim must be 1, 2 or 3 (got %d)", d->ndim);
+    if (d->dtype != CONV_DT_F32 && d->dtype != CONV_DT_BF16)
+        return fail(CONV_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+    if (d->has_bias != 0 && d->has_bias != 1) return fail(CONV_ERR_INVALID_ARG, "has_bias must be 0 or 1");
+    if (d->gelu != 0 && d->gelu != 1) return fail(CONV_ERR_INVALID_ARG, "gelu must be 0 or 1");
+    if (d->N < 0) return fail(CONV_ERR_INVALID_ARG, "N must be >= 0 (got %lld)", (long long)d->N);
+    if (d->G < 1 || d->C < 1 || d->K < 1)
+        return fail(CONV_ERR_INVALID_ARG, "G, C and K must be >= 1 (got %lld, %lld, %lld)",
+                    (long long)d->G, (long long)d->C, (long long)d->K);
+    static const char *dn[3] = {"D", "H", "W"};
+    for (int i = 0; i < 3; ++i) {
+        if (d->in[i] < 1 || d->filt[i] < 1 || d->stride[i] < 1 || d->dilation[i] < 1 || d->pad[i] < 0)
+            return fail(CONV_ERR_INVALID_ARG, "dim %s: need in, filt, stride, dilation >= 1 and pad >= 0", dn[i]);
+        if (i < 3 - d->ndim &&
+            (d->in[i] != 1 || d->filt[i] != 1 || d->stride[i] != 1 || d->dilation[i] != 1 || d->pad[i] != 0))
+            return fail(CONV_ERR_INVALID_ARG, "dim %s is unused for ndim=%d and must be trivial", dn[i], d->ndim);
+        if (d->in[i] > (1 << 30) || d->filt[i] > (1 << 30) || d->stride[i] > (1 << 30) ||
+            d->dilation[i] > (1 << 30) || d->pad[i] > (1 << 30))
+            return fail(CONV_ERR_UNSUPPORTED, "dim %s: a size above 2^30", dn[i]);
+        out[i] = extent(d->in[i], d->filt[i], d->stride[i], d->pad[i], d->dilation[i]);
+        if (out[i] < 1)
+            return fail(CONV_ERR_INVALID_ARG, "dim %s: the dilated filter (%lld) is larger than the padded input (%lld)",
+                        dn[i], (long long)(d->dilation[i] * (d->filt[i] - 1) + 1),
+                        (long long)(d->in[i] + 2 * d->pad[i]));
+    }
+    if (d->G > (1 << 30) || d->C > (1 << 30) || d->K > (1 << 30) || d->N > (1 << 30))
+        return fail(CONV_ERR_UNSUPPORTED, "N, G, C or K above 2^30");
+    // Every element offset the kernel forms, including the padding halo, must
+    // fit in a signed 32-bit integer.
+    const double lim = 2147483647.0;
+    const double gc = (double)d->G * (double)d->C, gk = (double)d->G * (double)d->K;
+    const double xpad = (double)std::max<int64_t>(d->N, 1) * (d->in[0] + 2.0 * d->pad[0] + d->stride[0] * 2.0 + d->dilation[0] * d->filt[0]) *
+                        (d->in[1] + 2.0 * d->pad[1] + d->stride[1] * 2.0 + d->dilation[1] * d->filt[1]) *
+                        (d->in[2] + 2.0 * d->pad[2] + d->stride[2] * 2.0 + d->dilation[2] * d->filt[2]) * gc;
+    const double welem = gk * d->C * (double)d->filt[0] * d->filt[1] * d->filt[2];
+    const double yelem = (double)d->N * out[0] * out[1] * out[2] * gk;
+    if (xpad >= lim || welem >= lim || yelem >= lim)
+        return fail(CONV_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
+    return CONV_OK;
+}
+
+// Analytic cost of one configuration (arbitrary units ~ seconds): the
+// workgroups are spread over the compute units in rounds; each round costs
+// the MFMA time of one tile at an efficiency that grows with the wave
+// sub-tile (larger sub-tiles read LDS less per flop); the whole run is at
+// least the time to move the algorithmic bytes at HBM speed.
+double cost(const TileCfg &c, const conv_fwd_plan &pl, int cus)
+{
+    const conv_fwd_desc_t &d = pl.desc;
+    const int64_t M = d.N * pl.out[0] * pl.out[1] * pl.out[2];
+    const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
+    const int64_t tm = (M + c.BM - 1) / c.BM, tn = (d.K + c.BN - 1) / c.BN;
+    const double tiles = (double)tm * tn * d.G;
+    const double kpad = (double)((Kred + c.BK - 1) / c.BK) * c.BK;
+    const double flop_tile = 2.0 * c.BM * c.BN * kpad;
+    const double cu_rate = (d.dtype == CONV_DT_BF16 ? 4096.0 : 256.0) * 2.4e9;  // flop/s per CU
+    const double tmw = (double)c.BM / c.WM, tnw = (double)c.BN / c.WN;
+    const double intensity = tmw * tnw / (tmw + tnw);                          // 8 .. 43
+    double eff = std::min(1.0, intensity / (d.dtype == CONV_DT_BF16 ? 40.0 : 12.0));
+    eff *= (double)(c.WM * c.WN) / 4.0;                                          // waves per CU
+    const double rounds = std::ceil(tiles / cus);
+    const double t_mfma = rounds * flop_tile / (cu_rate * std::max(eff, 0.05));
+    const double bytes = (double)pl.esz * (pl.x_elems + pl.w_elems + pl.b_elems + pl.y_elems);
+    const double t_mem = bytes / 8.0e12;
+    return std::max(t_mfma, t_mem) + 1e-7 * kpad / c.BK;  // small per-step overhead
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *conv_fwd_last_error(void) { return g_err; }
+
+int32_t conv_fwd_num_configs(void) { return kNumCfgs; }
+
+const char *conv_fwd_config_name(int32_t config)
+{
+    return (config >= 0 && config < kNumCfgs) ? kCfgs[config].name : nullptr;
+}
+
+int32_t conv_fwd_config_dtype(int32_t config)
+{
+    return (config >= 0 && config < kNumCfgs) ? kCfgs[config].dtype : -1;
+}
+
+static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, conv_fwd_plan_t **plan)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan output pointer is NULL");
+    *plan = nullptr;
+    int64_t out[3];
+    conv_status_t st = validate(desc, out);
+    if (st != CONV_OK) return st;
+
+    conv_fwd_plan *pl = new (std::nothrow) conv_fwd_plan();
+    if (!pl) return fail(CONV_ERR_NOMEM, "plan allocation failed");
+    const conv_fwd_desc_t &d = *desc;
+    pl->desc = d;
+    for (int i = 0; i < 3; ++i) pl->out[i] = out[i];
+    pl->esz = d.dtype == CONV_DT_BF16 ? 2 : 4;
+    pl->x_elems = d.N * d.in[0] * d.in[1] * d.in[2] * d.G * d.C;
+    pl->w_elems = d.G * d.K * d.filt[0] * d.filt[1] * d.filt[2] * d.C;
+    pl->b_elems = d.has_bias ? d.G * d.K : 0;
+    pl->y_elems = d.N * out[0] * out[1] * out[2] * d.G * d.K;
+
+    const int vec = 16 / pl->esz;
+    const int want_vec = (d.C % vec == 0) ? vec : 1;
+    if (forced >= 0) {
+        if (forced >= kNumCfgs) {
+            delete pl;
+            return fail(CONV_ERR_INVALID_ARG, "config %d out of range (0..%d)", forced, kNumCfgs - 1);
+        }
+        const TileCfg &c = kCfgs[forced];
+        if (c.dtype != d.dtype) {
+            delete pl;
+            return fail(CONV_ERR_UNSUPPORTED, "config %s is for the other dtype", c.name);
+        }
+        if (c.VEC != 1 && c.VEC != want_vec) {
+            delete pl;
+            return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)", c.name, c.VEC,
+                        (long long)d.C);
+        }
+        pl->cfg = forced;
+    } else {
+        const int cus = device_cu_count();
+        int best = -1;
+        double best_cost = 0.0;
+        for (int i = 0; i < kNumCfgs; ++i) {
+            const TileCfg &c = kCfgs[i];
+            if (c.dtype != d.dtype || c.VEC != want_vec) continue;
+            const double t = cost(c, *pl, cus);
+            if (best < 0 || t < best_cost) { best = i; best_cost = t; }
+        }
+        pl->cfg = best;
+    }
+    const TileCfg &c = kCfgs[pl->cfg];
+    KParams &kp = pl->kp;
+    kp.N = (int)d.N; kp.G = (int)d.G; kp.C = (int)d.C; kp.K = (int)d.K;
+    kp.Di = (int)d.in[0]; kp.Hi = (int)d.in[1]; kp.Wi = (int)d.in[2];
+    kp.Z = (int)d.filt[0]; kp.Y = (int)d.filt[1]; kp.X = (int)d.filt[2];
+    kp.sd = (int)d.stride[0]; kp.sh = (int)d.stride[1]; kp.sw = (int)d.stride[2];
+    kp.pd = (int)d.pad[0]; kp.ph = (int)d.pad[1]; kp.pw = (int)d.pad[2];
+    kp.dd = (int)d.dilation[0]; kp.dh = (int)d.dilation[1]; kp.dw = (int)d.dilation[2];
+    kp.Do = (int)out[0]; kp.Ho = (int)out[1]; kp.Wo = (int)out[2];
+    kp.M = (int)(d.N * out[0] * out[1] * out[2]);
+    kp.Kred = (int)(d.C * d.filt[0] * d.filt[1] * d.filt[2]);
+    kp.tiles_m = (kp.M + c.BM - 1) / c.BM;
+    kp.tiles_n = (kp.K + c.BN - 1) / c.BN;
+    kp.gelu = d.gelu;
+    kp.out_vec = (d.K % (16 / pl->esz) == 0) ? 1 : 0;
+    const double grid = (double)kp.tiles_m * kp.tiles_n * d.G;
+    if (grid >= 2147483647.0) {
+        delete pl;
+        return fail(CONV_ERR_UNSUPPORTED, "grid too large");
+    }
+    pl->grid = (int)grid;
+    snprintf(pl->text, sizeof(pl->text),
+             "igemm %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%dx%d tiles) lds=%dB%s",
+             c.name, kp.M, kp.K, kp.Kred, kp.G, pl->grid, kp.tiles_m, kp.tiles_n, kp.G, c.lds_bytes,
+             forced >= 0 ? " forced" : "");
+    if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
+    *plan = pl;
+    return CONV_OK;
+}
+
+conv_status_t conv_fwd_create(const conv_fwd_desc_t *desc, conv_fwd_plan_t **plan)
+{
+    return create_impl(desc, -1, plan);
+}
+
+conv_status_t conv_fwd_create_with_config(const conv_fwd_desc_t *desc, int32_t config, conv_fwd_plan_t **plan)
+{
+    if (config < 0) {
+        if (plan) *plan = nullptr;
+        return fail(CONV_ERR_INVALID_ARG, "config %d out of range", config);
+    }
+    return create_impl(desc, config, plan);
+}
+
+conv_status_t conv_fwd_out_dims(const conv_fwd_plan_t *plan, int64_t out[3])
+{
+    if (!plan || !out) return fail(CONV_ERR_INVALID_ARG, "NULL argument");
+    for (int i = 0; i < 3; ++i) out[i] = plan->out[i];
+    return CONV_OK;
+}
+
+static bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
+{
+    if (!a || !b || an <= 0 || bn <= 0) return false;
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + bn && pb < pa + an;
+}
+
+conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const void *w,
+                           const void *bias, void *y, void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    const conv_fwd_desc_t &d = plan->desc;
+    if (plan->desc.has_bias && !bias) return fail(CONV_ERR_INVALID_ARG, "plan has a bias but bias is NULL");
+    if (!plan->desc.has_bias && bias) return fail(CONV_ERR_INVALID_ARG, "plan has no bias but bias is not NULL");
+    if (!w) return fail(CONV_ERR_INVALID_ARG, "w is NULL");
+    if (plan->y_elems == 0) return CONV_OK;   // N = 0: nothing to do
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "x or y is NULL");
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "x, w and y must be 16-byte aligned");
+    if (bias && ((uintptr_t)bias & (uintptr_t)(plan->esz - 1)))
+        return fail(CONV_ERR_INVALID_ARG, "bias is not aligned to its element size");
+    const int64_t e = plan->esz;
+    if (overlaps(y, plan->y_elems * e, x, plan->x_elems * e) || overlaps(y, plan->y_elems * e, w, plan->w_elems * e) ||
+        overlaps(y, plan->y_elems * e, bias, plan->b_elems * e))
+        return fail(CONV_ERR_INVALID_ARG, "y overlaps an input");
+    KParams kp = plan->kp;
+    kp.x = x; kp.w = w; kp.bias = bias; kp.y = y;
+    (void)d;
+    (void)hipGetLastError();  // clear a stale error so the check below is ours
+    kCfgs[plan->cfg].fn(kp, plan->grid, (hipStream_t)stream);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+void conv_fwd_destroy(conv_fwd_plan_t *plan) { delete plan; }
+
+const char *conv_fwd_describe(const conv_fwd_plan_t *plan) { return plan ? plan->text : ""; }
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+/*
+ * convfwd -- forward convolution as implicit im2col + tiled MFMA GEMM on
+ * MI355X (gfx950).  C ABI.
+ *
+ * The operation (the ExecuTorch conv1d issue, sections "Describe the bug"
+ * and "Suggested fix": nn.Conv1d / nn.Conv2d / aten.convolution semantics,
+ * conv1d re-expressed as conv2d with a singleton height and run as im2col +
+ * GEMM; the Composable Kernel grouped-conv note, intro and section 2: grouped
+ * forward conv NHWGC x GKYXC -> NHWGK in 2-D and 3-D with per-dimension
+ * dilation):
+ *
+ *   y[n,od,oh,ow,g,k] = act( b[g,k] + sum_{z,y,x,c} x[n, od*sd-pd+z*dd,
+ *                              oh*sh-ph+y*dh, ow*sw-pw+x*dw, g, c] * w[g,k,z,y,x,c] )
+ *
+ * cross-correlation (no kernel flip), symmetric zero padding (out-of-range
+ * input positions contribute nothing), act = identity or the exact erf-GELU
+ * 0.5*v*erfc(-v/sqrt(2)).  Output extent per spatial dim:
+ *   O = floor((I + 2*p - d*(F-1) - 1) / s) + 1.
+ *
+ * Every problem is handled as a 3-D one: a 1-D conv is ndim = 1 with
+ * D = H = 1 (and Z = Y = 1), a 2-D conv is ndim = 2 with D = 1 (Z = 1).
+ *
+ * Layouts (row-major, last index fastest; C and K are PER GROUP):
+ *   x    : N x Di x Hi x Wi x G x C     (for 1-D: N x W x C when G = 1)
+ *   w    : G x K  x Z  x Y  x X x C     (for 1-D: K x X x C)
+ *   bias : G x K
+ *   y    : N x Do x Ho x Wo x G x K
+ * dtype CONV_DT_F32: x, w, bias, y are float32; products and sums in fp32
+ *                    (full-precision f32 MFMA).
+ * dtype CONV_DT_BF16: x, w, bias, y are bfloat16; products exact, sums in
+ *                    fp32, bias and GELU applied in fp32, the result rounded
+ *                    to bfloat16 nearest-even.
+ *
+ * Ownership: the caller owns every device buffer and the stream.  A plan
+ * holds host memory only, is immutable after creation and may be used from
+ * several threads and streams at once.  conv_fwd_run allocates nothing,
+ * does not synchronise and only enqueues work on the given stream.
+ *
+ * Errors: every call returns a status and never throws.  A thread-local
+ * message describing the last failure is returned by conv_fwd_last_error().
+ * Failures inside an already-enqueued kernel surface at the caller's next
+ * synchronisation of that stream.
+ */
+#ifndef CONVFWD_H
+#define CONVFWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONV_DT_F32 = 0,
+    CONV_DT_BF16 = 1
+} conv_dtype_t;
+
+typedef enum {
+    CONV_OK = 0,
+    CONV_ERR_INVALID_ARG = 1,  /* a value outside its documented range        */
+    CONV_ERR_UNSUPPORTED = 2,  /* valid, but beyond this library's limits      */
+    CONV_ERR_HIP = 3,          /* the HIP runtime reported an error            */
+    CONV_ERR_NOMEM = 4         /* host allocation of the plan failed           */
+} conv_status_t;
+
+/* Problem descriptor.  For ndim < 3 the unused leading spatial dims must be
+ * trivial: in = filt = stride = dilation = 1 and pad = 0. */
+typedef struct {
+    int32_t ndim;          /* 1, 2 or 3 spatial dims                          */
+    int32_t dtype;         /* conv_dtype_t                                     */
+    int64_t N;             /* batch, >= 0 (N = 0 is an empty, valid problem)   */
+    int64_t G;             /* groups, >= 1                                     */
+    int64_t C;             /* input channels per group, >= 1                   */
+    int64_t K;             /* output channels per group, >= 1                  */
+    int64_t in[3];         /* Di, Hi, Wi, >= 1                                 */
+    int64_t filt[3];       /* Z, Y, X, >= 1                                    */
+    int64_t stride[3];     /* >= 1                                             */
+    int64_t pad[3];        /* >= 0, same amount before and after               */
+    int64_t dilation[3];   /* >= 1                                             */
+    int32_t has_bias;      /* 0 or 1                                           */
+    int32_t gelu;          /* 0 or 1: apply exact erf-GELU after the bias      */
+} conv_fwd_desc_t;
+
+typedef struct conv_fwd_plan conv_fwd_plan_t;   /* opaque */
+
+/* Validates the descriptor on the host, computes the output extents, picks a
+ * tile configuration for the shape (per-shape selector) and returns an
+ * immutable plan in *plan.  Needs no GPU work; reads the current device's
+ * compute-unit count if a device is present.
+ *   CONV_ERR_INVALID_ARG : NULL pointer, ndim not 1..3, N < 0, G/C/K < 1,
+ *                          in/filt/stride/dilation < 1, pad < 0, a
+ *                          non-trivial unused dim, unknown dtype, has_bias or
+ *                          gelu not 0/1, or an empty output extent.
+ *   CONV_ERR_UNSUPPORTED : a tensor (x including its padding halo, w, y) of
+ *                          2^31 elements or more.
+ *   CONV_ERR_NOMEM       : plan allocation failed. */
+conv_status_t conv_fwd_create(const conv_fwd_desc_t *desc, conv_fwd_plan_t **plan);
+
+/* As conv_fwd_create, but forces tile configuration `config` (an index below
+ * conv_fwd_num_configs()).  CONV_ERR_UNSUPPORTED if that configuration is
+ * for the other dtype.  For sweeps and for testing every kernel variant. */
+conv_status_t conv_fwd_create_with_config(const conv_fwd_desc_t *desc, int32_t config,
+                                          conv_fwd_plan_t **plan);
+
+/* Writes (Do, Ho, Wo) of the plan's problem to out[3]. */
+conv_status_t conv_fwd_out_dims(const conv_fwd_plan_t *plan, int64_t out[3]);
+
+/* Enqueues y = conv(x, w) (+ bias) (then GELU) on `stream` (a hipStream_t;
+ * NULL = the null stream).  x, w, y: device pointers in the layouts above,
+ * 16-byte aligned; bias: device pointer, must be NULL iff the plan has no
+ * bias.  y must not overlap x, w or bias.
+ *   CONV_ERR_INVALID_ARG : NULL plan, a required NULL pointer, bias given or
+ *                          missing against has_bias, misalignment, overlap.
+ *   CONV_ERR_HIP         : the launch failed (message has the HIP text). */
+conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const void *w,
+                           const void *bias, void *y, void *stream);
+
+/* Frees a plan.  NULL is a no-op. */
+void conv_fwd_destroy(conv_fwd_plan_t *plan);
+
+/* Human-readable description of the plan's chosen kernel and grid; owned by
+ * the plan, valid until conv_fwd_destroy.  "" for NULL. */
+const char *conv_fwd_describe(const conv_fwd_plan_t *plan);
+
+/* Number of tile configurations compiled into the library, and the name and
+ * dtype of one (NULL / -1 for an index out of range). */
+int32_t conv_fwd_num_configs(void);
+const char *conv_fwd_config_name(int32_t config);
+int32_t conv_fwd_config_dtype(int32_t config);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *conv_fwd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVFWD_H */

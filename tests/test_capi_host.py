@@ -1,0 +1,201 @@
+"""Host-side tests of the C ABI: the library loads, exports every function
+include/convfwd.h declares, validates descriptors, and rejects bad run()
+arguments before launching anything.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from convolution_forward_implicit_amd import capi, desc_from_problem, ConvFwd, ConvError
+import synthdata as sd
+from oracle import ref
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "convfwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv_fwd_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_expects():
+    assert declared_functions() == sorted(capi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = capi.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_desc_struct_layout_matches_header():
+    # int32 ndim, int32 dtype, 4 int64, 5 x int64[3], int32 has_bias, int32 gelu
+    assert ctypes.sizeof(capi.conv_fwd_desc_t) == 8 + 4 * 8 + 15 * 8 + 8
+    assert capi.conv_fwd_desc_t.N.offset == 8
+    assert capi.conv_fwd_desc_t.has_bias.offset == 8 + 4 * 8 + 15 * 8
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_out_dims_match_oracle_at_every_workload(wid):
+    for p, hb, ge in sd.layers(wid):
+        plan = capi.conv_fwd_create(desc_from_problem(p, sd.dtype_of(wid), hb, ge))
+        try:
+            assert capi.conv_fwd_out_dims(plan) == ref.out_dims(p)
+            assert "igemm" in capi.conv_fwd_describe(plan)
+        finally:
+            capi.conv_fwd_destroy(plan)
+
+
+def test_out_dims_grid_against_oracle():
+    import itertools
+    for I, F, s, p, d in itertools.product((1, 2, 5, 9), (1, 2, 3), (1, 2, 3), (0, 1, 3), (1, 2)):
+        prob = sd.conv1d_problem(1, 1, 1, I, F, s, p, d)
+        try:
+            want = ref.out_dims(prob)
+        except ValueError:
+            with pytest.raises(ConvError) as e:
+                capi.conv_fwd_create(desc_from_problem(prob, "f32"))
+            assert e.value.status == capi.CONV_ERR_INVALID_ARG
+            continue
+        plan = capi.conv_fwd_create(desc_from_problem(prob, "f32"))
+        assert capi.conv_fwd_out_dims(plan) == want
+        capi.conv_fwd_destroy(plan)
+
+
+def _base(**kw):
+    args = dict(ndim=2, dtype="bf16", N=2, G=1, C=8, K=8, inp=(1, 5, 5), filt=(1, 3, 3),
+                stride=(1, 1, 1), pad=(0, 1, 1), dilation=(1, 1, 1))
+    args.update(kw)
+    return args
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ndim=0), capi.CONV_ERR_INVALID_ARG),
+    (dict(ndim=4), capi.CONV_ERR_INVALID_ARG),
+    (dict(dtype=7), capi.CONV_ERR_INVALID_ARG),
+    (dict(N=-1), capi.CONV_ERR_INVALID_ARG),
+    (dict(G=0), capi.CONV_ERR_INVALID_ARG),
+    (dict(C=0), capi.CONV_ERR_INVALID_ARG),
+    (dict(K=0), capi.CONV_ERR_INVALID_ARG),
+    (dict(inp=(1, 0, 5)), capi.CONV_ERR_INVALID_ARG),
+    (dict(filt=(1, 3, 0)), capi.CONV_ERR_INVALID_ARG),
+    (dict(stride=(1, 0, 1)), capi.CONV_ERR_INVALID_ARG),
+    (dict(dilation=(1, 1, 0)), capi.CONV_ERR_INVALID_ARG),
+    (dict(pad=(0, -1, 0)), capi.CONV_ERR_INVALID_ARG),
+    (dict(inp=(2, 5, 5)), capi.CONV_ERR_INVALID_ARG),          # unused D dim not trivial
+    (dict(pad=(1, 1, 1)), capi.CONV_ERR_INVALID_ARG),
+    (dict(filt=(1, 9, 3)), capi.CONV_ERR_INVALID_ARG),         # empty output
+    (dict(N=1 << 20, inp=(1, 1024, 1024), C=64), capi.CONV_ERR_UNSUPPORTED),
+    (dict(C=1 << 16, K=1 << 16, filt=(1, 3, 3)), capi.CONV_ERR_UNSUPPORTED),
+])
+def test_create_rejects_invalid(kw, status):
+    a = _base(**kw)
+    d = capi.make_desc(a["ndim"], a["dtype"] if isinstance(a["dtype"], str) else a["dtype"],
+                       a["N"], a["G"], a["C"], a["K"], a["inp"], a["filt"], a["stride"],
+                       a["pad"], a["dilation"])
+    with pytest.raises(ConvError) as e:
+        capi.conv_fwd_create(d)
+    assert e.value.status == status
+    assert capi.conv_fwd_last_error()
+
+
+def test_flags_must_be_boolean():
+    d = desc_from_problem(sd.conv1d_problem(1, 4, 4, 8, 3, 1, 1), "f32")
+    d.has_bias = 2
+    with pytest.raises(ConvError):
+        capi.conv_fwd_create(d)
+    d.has_bias, d.gelu = 0, 5
+    with pytest.raises(ConvError):
+        capi.conv_fwd_create(d)
+
+
+def test_null_arguments():
+    lib = capi.lib()
+    assert lib.conv_fwd_create(None, None) == capi.CONV_ERR_INVALID_ARG
+    d = desc_from_problem(sd.conv1d_problem(1, 4, 4, 8, 3, 1, 1), "f32")
+    assert lib.conv_fwd_create(ctypes.byref(d), None) == capi.CONV_ERR_INVALID_ARG
+    assert lib.conv_fwd_out_dims(None, None) == capi.CONV_ERR_INVALID_ARG
+    assert lib.conv_fwd_run(None, None, None, None, None, None) == capi.CONV_ERR_INVALID_ARG
+    lib.conv_fwd_destroy(None)                       # no-op
+    assert lib.conv_fwd_describe(None) == b""
+
+
+def test_config_table():
+    n = capi.conv_fwd_num_configs()
+    assert n >= 2
+    names = [capi.conv_fwd_config_name(i) for i in range(n)]
+    assert len(set(names)) == n
+    assert {capi.conv_fwd_config_dtype(i) for i in range(n)} == {0, 1}
+    assert capi.conv_fwd_config_name(n) is None and capi.conv_fwd_config_dtype(-1) == -1
+
+
+def test_forced_config_dtype_and_vector_rules():
+    n = capi.conv_fwd_num_configs()
+    d_bf16 = desc_from_problem(sd.problem(1, 1, 16, 16, (1, 6, 6), (1, 3, 3)), "bf16")
+    d_odd = desc_from_problem(sd.problem(1, 1, 5, 16, (1, 6, 6), (1, 3, 3)), "bf16")
+    for i in range(n):
+        name = capi.conv_fwd_config_name(i)
+        if capi.conv_fwd_config_dtype(i) != capi.CONV_DT_BF16:
+            with pytest.raises(ConvError) as e:
+                capi.conv_fwd_create_with_config(d_bf16, i)
+            assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+            continue
+        plan = capi.conv_fwd_create_with_config(d_bf16, i)
+        assert name in capi.conv_fwd_describe(plan)
+        capi.conv_fwd_destroy(plan)
+        if not name.endswith("_v1"):   # 16-byte channel vectors need C % 8 == 0
+            with pytest.raises(ConvError):
+                capi.conv_fwd_create_with_config(d_odd, i)
+    with pytest.raises(ConvError):
+        capi.conv_fwd_create_with_config(d_bf16, n)
+    with pytest.raises(ConvError):
+        capi.conv_fwd_create_with_config(d_bf16, -1)
+
+
+def test_selector_uses_scalar_loads_only_for_odd_channels():
+    for C, dt, vec_ok in ((80, "f32", True), (6, "f32", False), (64, "bf16", True), (12, "bf16", False)):
+        c = ConvFwd(sd.conv1d_problem(1, C, 8, 50, 3, 1, 1), dt)
+        assert c.describe().split()[1].endswith("_v1") != vec_ok, c.describe()
+
+
+def test_run_argument_checks_before_launch():
+    """Every failure below is detected on the host; nothing is launched."""
+    lib = capi.lib()
+    p = sd.conv1d_problem(1, 8, 8, 16, 3, 1, 1)
+    plan_b = capi.conv_fwd_create(desc_from_problem(p, "f32", has_bias=True))
+    plan = capi.conv_fwd_create(desc_from_problem(p, "f32"))
+    A = 1 << 20   # fake, well-separated, aligned addresses: never dereferenced
+    try:
+        assert lib.conv_fwd_run(plan_b, A, 2 * A, None, 3 * A, None) == capi.CONV_ERR_INVALID_ARG
+        assert lib.conv_fwd_run(plan, A, 2 * A, 4 * A, 3 * A, None) == capi.CONV_ERR_INVALID_ARG
+        assert lib.conv_fwd_run(plan, None, 2 * A, None, 3 * A, None) == capi.CONV_ERR_INVALID_ARG
+        assert lib.conv_fwd_run(plan, A, None, None, 3 * A, None) == capi.CONV_ERR_INVALID_ARG
+        assert lib.conv_fwd_run(plan, A, 2 * A, None, None, None) == capi.CONV_ERR_INVALID_ARG
+        assert lib.conv_fwd_run(plan, A + 4, 2 * A, None, 3 * A, None) == capi.CONV_ERR_INVALID_ARG
+        assert "aligned" in capi.conv_fwd_last_error()
+        assert lib.conv_fwd_run(plan, A, 2 * A, None, A + 64, None) == capi.CONV_ERR_INVALID_ARG
+        assert "overlap" in capi.conv_fwd_last_error()
+        assert lib.conv_fwd_run(plan_b, A, 2 * A, 3 * A + 2, 4 * A, None) == capi.CONV_ERR_INVALID_ARG
+    finally:
+        capi.conv_fwd_destroy(plan)
+        capi.conv_fwd_destroy(plan_b)
+
+
+def test_empty_batch_is_a_valid_noop():
+    p = sd.conv1d_problem(0, 8, 8, 16, 3, 1, 1)
+    plan = capi.conv_fwd_create(desc_from_problem(p, "bf16"))
+    try:
+        assert capi.conv_fwd_out_dims(plan) == (1, 1, 16)
+        # nothing to compute: returns before touching the device
+        assert capi.lib().conv_fwd_run(plan, None, 1 << 20, None, None, None) == capi.CONV_OK
+    finally:
+        capi.conv_fwd_destroy(plan)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(capi, "_lib", None)
+    monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "libconvfwd.so"))
+    with pytest.raises(ImportError):
+        capi.lib()

@@ -1,0 +1,239 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Tolerance (oracle/check.py): |g - r| <= rtol*|r| + L*gamma_n*sum|x*w|, with
+rtol 1e-4 (fp32 outputs) or 8e-3 (bf16 outputs).  Integer-valued inputs in
+{-2..2} make every fp32 sum exact in any order, so those cases are compared
+bit for bit (bf16 outputs against the one nearest-even rounding of the exact
+value)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import synthdata as sd
+from oracle import ref, check
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype, dev):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return t if dtype == "f32" else t.to(torch.bfloat16)
+
+
+def host(y):
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def bits(y):
+    return y.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(dev, p, dtype, x, w, b, gelu, config=None, out=None):
+    from convolution_forward_implicit_amd import ConvFwd
+    c = ConvFwd(p, dtype, b is not None, gelu, config=config)
+    print("case:", p, dtype, "gelu" if gelu else "", c.describe(), flush=True)
+    y = c(to_dev(x, dtype, dev), to_dev(w, dtype, dev),
+          None if b is None else to_dev(b, dtype, dev), out=out)
+    torch.cuda.synchronize()
+    return y, c
+
+
+def sample_indices(p, n, seed):
+    """Random flat output indices plus every combination of border/centre
+    output coordinates (first, second, middle, second-to-last, last)."""
+    _, _, _, ys = ref.shapes(p)
+    total = int(np.prod(ys))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = list(rng.integers(0, total, n))
+    pick = lambda O: sorted({0, min(1, O - 1), O // 2, max(O - 2, 0), O - 1})
+    N, Do, Ho, Wo, G, K = ys
+    for nb, od, oh, ow in itertools.product(pick(N), pick(Do), pick(Ho), pick(Wo)):
+        for g, k in ((0, 0), (G - 1, K - 1), (int(rng.integers(G)), int(rng.integers(K)))):
+            idx.append(((((nb * Do + od) * Ho + oh) * Wo + ow) * G + g) * K + k)
+    return np.unique(np.array(idx, dtype=np.int64))
+
+
+def assert_close(got, p, dtype, x, w, b, gelu, idx=None):
+    if idx is None:
+        r, a = ref.conv_fwd(p, x, w, b, gelu)
+        g = got
+    else:
+        r, a = ref.conv_fwd_points(p, x, w, b, gelu, idx)
+        g = got.ravel()[idx]
+    st = check.check(g, r, a, p, dtype, b is not None, gelu)
+    print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine", "max_abs_diff")},
+          flush=True)
+    assert st["ok"], st
+    return st
+
+
+# --------------------------------------------------------------------------
+# The five workloads at full size, in the launch configuration the benchmark
+# times (the selector's choice).
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_workload_seeded_parity(dev, wid):
+    W = sd.workload(wid)
+    dt = W["dtype"]
+    x = W["x"]
+    for li, (p, hb, ge) in enumerate(W["layers"]):
+        y, c = run(dev, p, dt, x, W["w"][li], W["b"][li], ge)
+        full = ref.useful_flop(p) < 2e9
+        idx = None if full else sample_indices(p, 4000, 100 + wid * 10 + li)
+        assert_close(host(y), p, dt, x, W["w"][li], W["b"][li], ge, idx)
+        x = host(y).astype(np.float32)   # next layer is graded on the device's own input
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_workload_integer_bit_exact(dev, wid):
+    W = sd.workload(wid)
+    dt = W["dtype"]
+    for li, (p, hb, _) in enumerate(W["layers"]):
+        x, w, b = sd.random_inputs(p, dt, 500 + wid * 10 + li, hb, kind="int")
+        y, _ = run(dev, p, dt, x, w, b, False)
+        full = ref.useful_flop(p) < 2e9
+        idx = None if full else sample_indices(p, 4000, 7 + li)
+        r = ref.conv_fwd(p, x, w, b, False, want_absdot=False)
+        r = r.ravel() if idx is None else r.ravel()[idx]
+        if dt == "f32":
+            g = host(y).ravel()
+            g = g if idx is None else g[idx]
+            assert np.array_equal(g, r)
+        else:
+            g = bits(y).ravel()
+            g = g if idx is None else g[idx]
+            assert np.array_equal(g, check.round_to_bf16_bits(r))
+
+
+# --------------------------------------------------------------------------
+# Every compiled tile configuration on problems that span several tiles and
+# end in ragged tails along M, N (=K) and the reduction.
+def _configs():
+    from convolution_forward_implicit_amd import capi
+    try:
+        n = capi.conv_fwd_num_configs()
+    except ImportError:
+        return []
+    return [(i, capi.conv_fwd_config_name(i)) for i in range(n)]
+
+
+CONFIGS = _configs()
+
+
+def _ragged_problem(name):
+    C = 5 if name.endswith("_v1") else 24
+    # 2-D, M = 2*13*11 = 286, K = 40, Kred = 9*C (216 or 45), G = 2
+    return sd.problem(2, 2, C, 40, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1))
+
+
+@pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
+def test_every_config_ragged(dev, cfg, name):
+    dt = "bf16" if name.startswith("bf16") else "f32"
+    p = _ragged_problem(name)
+    x, w, b = sd.random_inputs(p, dt, 31, True)
+    y, c = run(dev, p, dt, x, w, b, True, config=cfg)
+    assert name in c.describe()
+    assert_close(host(y), p, dt, x, w, b, True)
+    xi, wi, bi = sd.random_inputs(p, dt, 32, True, kind="int")
+    y, _ = run(dev, p, dt, xi, wi, bi, False, config=cfg)
+    r = ref.conv_fwd(p, xi, wi, bi, False, want_absdot=False)
+    if dt == "f32":
+        assert np.array_equal(host(y), r)
+    else:
+        assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
+
+
+@pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
+def test_every_config_3d_strided_dilated(dev, cfg, name):
+    dt = "bf16" if name.startswith("bf16") else "f32"
+    C = 3 if name.endswith("_v1") else 16
+    p = sd.problem(3, 3, C, 20, (5, 9, 8), (3, 2, 3), (2, 1, 2), (2, 1, 3), (2, 3, 1))
+    x, w, b = sd.random_inputs(p, dt, 33, False)
+    y, _ = run(dev, p, dt, x, w, None, False, config=cfg)
+    assert_close(host(y), p, dt, x, w, None, False)
+
+
+# --------------------------------------------------------------------------
+# Edge cases (selector's choice)
+EDGE = [
+    ("c1_k1_conv1d", sd.conv1d_problem(2, 1, 1, 100, 3, 1, 1)),
+    ("odd_channels", sd.conv1d_problem(3, 3, 5, 77, 5, 2, 2)),
+    ("stride_gt_filter", sd.problem(2, 1, 16, 24, (1, 17, 19), (1, 2, 2), (1, 3, 3), (0, 0, 1))),
+    ("one_by_one_output", sd.problem(5, 1, 32, 16, (1, 3, 3), (1, 3, 3))),
+    ("pad_wider_than_filter", sd.conv1d_problem(2, 8, 8, 4, 3, 1, 3)),
+    ("dilation_and_pad_3d", sd.problem(1, 2, 8, 8, (7, 6, 9), (2, 3, 2), (1, 2, 1), (3, 2, 1), (3, 1, 4))),
+    ("k_not_vector_multiple", sd.problem(2, 3, 16, 13, (1, 9, 9), (1, 3, 3), (1, 1, 1), (0, 1, 1))),
+    ("many_groups", sd.problem(2, 32, 8, 8, (1, 10, 10), (1, 3, 3), (1, 1, 1), (0, 1, 1))),
+    ("pointwise_large_k", sd.problem(1, 1, 64, 520, (1, 7, 9), (1, 1, 1))),
+    ("long_1d_batch1", sd.conv1d_problem(1, 8, 16, 5003, 7, 1, 3)),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,p", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(dev, name, p, dt):
+    x, w, b = sd.random_inputs(p, dt, 41, True)
+    y, _ = run(dev, p, dt, x, w, b, True)
+    assert_close(host(y), p, dt, x, w, b, True)
+    xi, wi, bi = sd.random_inputs(p, dt, 42, True, kind="int")
+    y, _ = run(dev, p, dt, xi, wi, bi, False)
+    r = ref.conv_fwd(p, xi, wi, bi, False, want_absdot=False)
+    if dt == "f32":
+        assert np.array_equal(host(y), r)
+    else:
+        assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
+
+
+def test_empty_batch_leaves_output_untouched(dev):
+    from convolution_forward_implicit_amd import ConvFwd
+    p = sd.conv1d_problem(0, 8, 8, 16, 3, 1, 1)
+    c = ConvFwd(p, "bf16")
+    x = torch.empty((0, 1, 1, 16, 1, 8), dtype=torch.bfloat16, device=dev)
+    w = torch.ones((1, 8, 1, 1, 3, 8), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((0, 1, 1, 16, 1, 8), dtype=torch.bfloat16, device=dev)
+    assert c(x, w, out=y) is y
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# Closed forms on the device: delta kernel and all-ones (exact in every dtype)
+@pytest.mark.parametrize("wid", [1, 4, 5])
+def test_delta_kernel_on_device(dev, wid):
+    p = dict(sd.layers(wid)[0][0], N=1)
+    dt = sd.dtype_of(wid)
+    xs, ws, _, _ = ref.shapes(p)
+    x, _, _ = sd.random_inputs(p, dt, 51, False)
+    w = np.zeros(ws, dtype=np.float32)
+    t0 = tuple(f - 1 for f in p["filt"])      # last tap: off-centre in every used dim
+    for k in range(p["K"]):
+        w[:, k, t0[0], t0[1], t0[2], k % p["C"]] = 1.0
+    y, _ = run(dev, p, dt, x, w, None, False)
+    r = ref.conv_fwd(p, x, w, None, False, want_absdot=False)
+    assert np.array_equal(host(y), r)
+
+
+@pytest.mark.parametrize("wid", [1, 4, 5])
+def test_all_ones_on_device(dev, wid):
+    p = dict(sd.layers(wid)[0][0], N=1)
+    dt = sd.dtype_of(wid)
+    xs, ws, _, _ = ref.shapes(p)
+    y, _ = run(dev, p, dt, np.ones(xs, np.float32), np.ones(ws, np.float32), None, False)
+    r = ref.conv_fwd(p, np.ones(xs), np.ones(ws), None, False, want_absdot=False)
+    assert np.array_equal(host(y), r)
+
+
+def test_repeat_runs_bitwise_identical(dev):
+    W = sd.workload(4)
+    p, _, _ = W["layers"][0]
+    y1, c = run(dev, p, "bf16", W["x"], W["w"][0], None, False)
+    y2 = c(to_dev(W["x"], "bf16", dev), to_dev(W["w"][0], "bf16", dev))
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
