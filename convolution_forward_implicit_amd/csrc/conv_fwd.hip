@@ -22,6 +22,7 @@
 
 #include "../../include/convfwd.h"
 #include "igemm_kernel.h"
+#include "igemm_dma.h"
 
 namespace convfwd {
 namespace {
@@ -37,34 +38,83 @@ conv_status_t fail(conv_status_t st, const char *fmt, ...)
     return st;
 }
 
-typedef void (*launch_fn)(const KParams &, int grid, hipStream_t);
+typedef void (*launch_fn)(const KParams &, uint32_t x_bytes, uint32_t w_bytes, int grid, hipStream_t);
 
 template <int DT, int BM, int BN, int BK, int WM, int WN, int VEC>
-void launch(const KParams &kp, int grid, hipStream_t s)
+void launch_reg(const KParams &kp, uint32_t, uint32_t, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL((igemm_fwd_kernel<DT, BM, BN, BK, WM, WN, VEC>), dim3(grid),
                        dim3(WM * WN * 64), 0, s, kp);
 }
 
+// The epilogue (bias, GELU) is compiled into each kernel variant, so a
+// variant carries only the code it runs.
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB>
+void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s)
+{
+    DmaParams dp;
+    dp.k = kp;
+    dp.x_bytes = xb;
+    dp.w_bytes = wb;
+    const dim3 g(grid), b(WM * WN * 64);
+    const bool bias = kp.bias != nullptr;
+    if (bias && kp.gelu)
+        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, true>), g, b, 0, s, dp);
+    else if (bias)
+        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, false>), g, b, 0, s, dp);
+    else if (kp.gelu)
+        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, true>), g, b, 0, s, dp);
+    else
+        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, false>), g, b, 0, s, dp);
+}
+
 struct TileCfg {
     int dtype;          // conv_dtype_t
-    int BM, BN, BK, WM, WN, VEC;
+    int dma;            // 1: direct global->LDS pipeline, 0: register-staged
+    int BM, BN, BK, WM, WN, VEC, NS;
     int lds_bytes;
     launch_fn fn;
     const char *name;
 };
 
 #define CFG(DT, BM, BN, BK, WM, WN, VEC)                                                 \
-    TileCfg{DT, BM, BN, BK, WM, WN, VEC,                                                 \
+    TileCfg{DT, 0, BM, BN, BK, WM, WN, VEC, 2,                                           \
             IgemmShape<DT, BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                          \
-            &launch<DT, BM, BN, BK, WM, WN, VEC>,                                        \
+            &launch_reg<DT, BM, BN, BK, WM, WN, VEC>,                                    \
             (DT ? "bf16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC                 \
                 : "f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC)}
+
+#define DMA(DT, BM, BN, WM, WN, NS, MF, KSUB)                                            \
+    TileCfg{DT, 1, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS,     \
+            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB>::LDS_BYTES,                        \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB>,                               \
+            (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB  \
+                : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB)}
 
 // One candidate table, shared by the selector, forced-config creation and
 // the sweeps.  VEC = 16 bytes of channels per load; the VEC = 1 entries serve
 // channel counts that are not a multiple of the vector.
 const TileCfg kCfgs[] = {
+    DMA(1, 128, 128, 2, 2, 2, 32, 1),
+    DMA(1, 128, 128, 2, 2, 2, 32, 2),
+    DMA(1, 256, 64, 4, 1, 2, 32, 1),
+    DMA(1, 128, 64, 2, 2, 2, 32, 1),
+    DMA(1, 128, 64, 2, 2, 2, 32, 2),
+    DMA(1, 128, 32, 4, 1, 2, 32, 1),
+    DMA(1, 64, 64, 2, 2, 2, 16, 1),
+    DMA(1, 64, 64, 2, 2, 2, 16, 2),
+    DMA(1, 128, 64, 2, 2, 2, 16, 1),
+    DMA(1, 128, 32, 4, 1, 2, 16, 1),
+    DMA(1, 128, 32, 4, 1, 2, 16, 2),
+    DMA(1, 64, 32, 2, 2, 2, 16, 2),
+    DMA(0, 32, 32, 2, 2, 2, 16, 1),
+    DMA(0, 32, 32, 2, 2, 2, 16, 2),
+    DMA(0, 32, 32, 2, 2, 2, 16, 4),
+    DMA(0, 32, 64, 1, 4, 2, 16, 1),
+    DMA(0, 32, 64, 1, 4, 2, 16, 2),
+    DMA(0, 64, 32, 4, 1, 2, 16, 2),
+    DMA(0, 64, 64, 2, 2, 2, 16, 1),
+    DMA(0, 64, 64, 2, 2, 2, 16, 2),
     CFG(1, 128, 128, 64, 2, 2, 8),
     CFG(1, 128, 64, 64, 2, 2, 8),
     CFG(1, 128, 32, 64, 4, 1, 8),
@@ -80,6 +130,25 @@ const TileCfg kCfgs[] = {
     CFG(0, 64, 64, 16, 2, 2, 1),
 };
 constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
+
+// Per-configuration cost coefficients fitted to a sweep of every
+// configuration over a grid of problems (tuning/fit.py): predicted
+// milliseconds t = a + b*r + d*r*nk, r = workgroups per compute unit, nk =
+// K-steps per workgroup.
+struct CostCoef {
+    const char *name;
+    double a, b, d;
+};
+const CostCoef kCoef[] = {
+#include "selector_coef.inc"
+};
+
+const CostCoef *coef_of(const TileCfg &c)
+{
+    for (const CostCoef &k : kCoef)
+        if (strcmp(k.name, c.name) == 0) return &k;
+    return nullptr;
+}
 
 int device_cu_count()
 {
@@ -160,7 +229,8 @@ conv_status_t validate(const conv_fwd_desc_t *d, int64_t out[3])
     return CONV_OK;
 }
 
-// Analytic cost of one configuration (arbitrary units ~ seconds): the
+// Analytic cost of one configuration (seconds), used for configurations the
+// calibration sweep has no coefficients for: the
 // workgroups are spread over the compute units in rounds; each round costs
 // the MFMA time of one tile at an efficiency that grows with the wave
 // sub-tile (larger sub-tiles read LDS less per flop); the whole run is at
@@ -179,11 +249,26 @@ double cost(const TileCfg &c, const conv_fwd_plan &pl, int cus)
     const double intensity = tmw * tnw / (tmw + tnw);                          // 8 .. 43
     double eff = std::min(1.0, intensity / (d.dtype == CONV_DT_BF16 ? 40.0 : 12.0));
     eff *= (double)(c.WM * c.WN) / 4.0;                                          // waves per CU
+    if (c.dma) eff = std::min(1.0, eff * 2.0);                                   // no register staging
     const double rounds = std::ceil(tiles / cus);
     const double t_mfma = rounds * flop_tile / (cu_rate * std::max(eff, 0.05));
     const double bytes = (double)pl.esz * (pl.x_elems + pl.w_elems + pl.b_elems + pl.y_elems);
     const double t_mem = bytes / 8.0e12;
     return std::max(t_mfma, t_mem) + 1e-7 * kpad / c.BK;  // small per-step overhead
+}
+
+// Predicted milliseconds of one configuration on the plan's problem.
+double predicted_ms(const TileCfg &c, const conv_fwd_plan &pl, int cus)
+{
+    const CostCoef *k = coef_of(c);
+    if (!k) return 1e3 * cost(c, pl, cus) * 10.0;   // uncalibrated: last resort
+    const conv_fwd_desc_t &d = pl.desc;
+    const int64_t M = d.N * pl.out[0] * pl.out[1] * pl.out[2];
+    const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
+    const double tiles = (double)((M + c.BM - 1) / c.BM) * (double)((d.K + c.BN - 1) / c.BN) * (double)d.G;
+    const double r = std::ceil(tiles / cus);
+    const double nk = (double)((Kred + c.BK - 1) / c.BK);
+    return k->a + k->b * r + k->d * r * nk;
 }
 
 }  // namespace
@@ -225,6 +310,12 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
 
     const int vec = 16 / pl->esz;
     const int want_vec = (d.C % vec == 0) ? vec : 1;
+    // the direct-to-LDS kernels address x and w with 32-bit byte offsets
+    const bool dma_ok = want_vec == vec && pl->x_elems * pl->esz < (int64_t(1) << 31) &&
+                        pl->w_elems * pl->esz < (int64_t(1) << 31);
+    auto eligible = [&](const TileCfg &c) {
+        return c.dtype == d.dtype && (c.dma ? dma_ok : c.VEC == want_vec);
+    };
     if (forced >= 0) {
         if (forced >= kNumCfgs) {
             delete pl;
@@ -235,10 +326,10 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
             delete pl;
             return fail(CONV_ERR_UNSUPPORTED, "config %s is for the other dtype", c.name);
         }
-        if (c.VEC != 1 && c.VEC != want_vec) {
+        if (c.VEC != 1 && !eligible(c)) {
             delete pl;
-            return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)", c.name, c.VEC,
-                        (long long)d.C);
+            return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)%s", c.name, c.VEC,
+                        (long long)d.C, c.dma ? " and x, w below 2 GiB" : "");
         }
         pl->cfg = forced;
     } else {
@@ -247,8 +338,8 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         double best_cost = 0.0;
         for (int i = 0; i < kNumCfgs; ++i) {
             const TileCfg &c = kCfgs[i];
-            if (c.dtype != d.dtype || c.VEC != want_vec) continue;
-            const double t = cost(c, *pl, cus);
+            if (!eligible(c)) continue;
+            const double t = predicted_ms(c, *pl, cus);
             if (best < 0 || t < best_cost) { best = i; best_cost = t; }
         }
         pl->cfg = best;
@@ -333,7 +424,8 @@ conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const voi
     kp.x = x; kp.w = w; kp.bias = bias; kp.y = y;
     (void)d;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    kCfgs[plan->cfg].fn(kp, plan->grid, (hipStream_t)stream);
+    kCfgs[plan->cfg].fn(kp, (uint32_t)(plan->x_elems * e), (uint32_t)(plan->w_elems * e), plan->grid,
+                        (hipStream_t)stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return CONV_OK;

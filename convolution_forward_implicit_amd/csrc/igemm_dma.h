@@ -1,0 +1,400 @@
+// Implicit-GEMM forward convolution for gfx950 with direct global->LDS loads.
+//
+// Same GEMM view as igemm_kernel.h (rows m = output pixels with the batch
+// folded in, columns n = output channels, reduction r = ((z*Y + y)*X + x)*C
+// + c), but the gathered im2col slices never pass through registers:
+//
+//  * every K-step moves one 128-byte slice of the reduction (64 bf16 or 32
+//    fp32 values) per tile row with `buffer_load_dwordx4 ... lds`: each lane
+//    fetches one 16-byte chunk and the hardware writes the 64 chunks of a
+//    wave to 1 KB of LDS in lane order (8 rows x 128 bytes);
+//  * padding needs no branch: an out-of-range tap gets a byte offset beyond
+//    the buffer's size and the buffer unit returns zeros;
+//  * NS LDS stages are in flight: step it+NS-1 is being fetched while step
+//    it is multiplied; the wait before a step names exactly how many newer
+//    loads may still be outstanding;
+//  * chunk q of row r is stored at 16-byte slot q ^ (r & 7), so the 8 lanes
+//    that read one 16-byte column of 8 consecutive rows hit 8 different
+//    bank groups;
+//  * the filter-tap position of a lane's chunk advances incrementally from
+//    step to step (no integer division in the loop).
+//
+// The loads are issued from inline assembly so that the compiler, which
+// cannot see which LDS bytes such a load writes, does not serialise every
+// LDS read behind every outstanding load; the waits are placed here by hand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "igemm_kernel.h"
+
+namespace convfwd {
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+struct DmaParams {
+    KParams k;
+    uint32_t x_bytes;   // buffer sizes: loads at or beyond them return zeros
+    uint32_t w_bytes;
+};
+
+constexpr uint32_t kOutOfRange = 0x80000000u;   // >= every buffer size accepted
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4_t r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xffffu);   // stride 0
+    r[2] = (int)bytes;                              // num_records (bytes)
+    r[3] = 0x00020000;                              // raw 32-bit data format
+    return r;
+}
+
+// One 16-byte-per-lane load into LDS at lds_addr + 16 * lane.  M0 carries
+// the LDS address and is restored afterwards.
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr)
+{
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds_addr)
+        : "memory");
+}
+
+// s_waitcnt that waits only on vmcnt (expcnt and lgkmcnt left at their max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB>
+struct DmaShape {
+    using T = typename Elem<DT>::type;
+    static constexpr int ESZ = (int)sizeof(T);
+    static constexpr int VEC = 16 / ESZ;          // elements per 16-byte chunk
+    static constexpr int SUBK = 128 / ESZ;        // reduction elements per 128-byte sub-slice
+    static constexpr int BK = SUBK * KSUB;        // reduction elements per K-step
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int MI = TM / MF, NI = TN / MF;   // MFMA blocks per wave
+    static constexpr int ACC = MF * MF / 64;          // accumulator floats per lane and block
+    static constexpr int A_PER_W = BM / 8 / NW;  // 8-row DMA blocks per wave and stage
+    static constexpr int B_PER_W = BN / 8 / NW;
+    static constexpr int L = (A_PER_W + B_PER_W) * KSUB;  // DMA loads per wave and stage
+    static constexpr int SUB = (BM + BN) * 128;   // bytes of one sub-slice (A rows then B rows)
+    static constexpr int STAGE = SUB * KSUB;
+    static constexpr int LDC = BN + VEC;
+    static constexpr int EPI = BM * LDC * ESZ;
+    static constexpr int LDS_BYTES = NS * STAGE > EPI ? NS * STAGE : EPI;
+
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole DMA blocks per wave");
+    static_assert(TM % MF == 0 && TN % MF == 0, "whole MFMA blocks per wave");
+    static_assert(MF == 16 || (MF == 32 && DT == 1), "32x32 blocks: bf16 only");
+    static_assert(NS >= 2 && L * (NS - 2) < 64, "vmcnt budget");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+};
+
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, bool BIAS, bool GELU>
+__global__ void __launch_bounds__(WM * WN * 64)
+igemm_dma_kernel(DmaParams dp)
+{
+    using S = DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB>;
+    using AccT = typename std::conditional<MF == 32, f32x16_t, f32x4_t>::type;
+    using T = typename S::T;
+    const KParams &p = dp.k;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS_BYTES];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+
+    // Workgroups are handed to the 8 XCDs round-robin; give each XCD a
+    // contiguous run of tiles so neighbouring output rows (which share input
+    // halo rows) meet in the same L2.
+    const int nb = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = nb >> 3, rem = nb & 7;
+    int bid = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int m_tile = bid % p.tiles_m;
+    bid /= p.tiles_m;
+    const int n_tile = bid % p.tiles_n;
+    const int g = bid / p.tiles_n;
+    const int m0 = m_tile * BM;
+    const int n0 = n_tile * BN;
+
+    const i32x4_t xr = buffer_rsrc(p.x, dp.x_bytes);
+    const i32x4_t wr = buffer_rsrc(p.w, dp.w_bytes);
+    const int GC = p.G * p.C;
+
+    // ---- this lane's DMA assignment -------------------------------------
+    const int lrow = lane >> 3;                 // row inside an 8-row block
+    const int chunk = (lane & 7) ^ lrow;        // which 16-byte chunk of the K slice
+
+    // Rows of this lane: m_t = m0 + (wave*A_PER_W + t)*8 + lrow.  The first
+    // is decoded with divisions, the others by stepping 8 pixels forward.
+    int a_off[S::A_PER_W], a_bd[S::A_PER_W], a_bh[S::A_PER_W], a_bw[S::A_PER_W];
+    {
+        const int mfirst = m0 + wave * S::A_PER_W * 8 + lrow;
+        int q = mfirst;
+        int ow = q % p.Wo; q /= p.Wo;
+        int oh = q % p.Ho; q /= p.Ho;
+        int od = q % p.Do;
+        int nb_ = q / p.Do;
+#pragma unroll
+        for (int t = 0; t < S::A_PER_W; ++t) {
+            const int m = mfirst + t * 8;
+            int bd = -(1 << 28), bh = 0, bw = 0, off = 0;
+            if (m < p.M) {
+                bd = od * p.sd - p.pd;
+                bh = oh * p.sh - p.ph;
+                bw = ow * p.sw - p.pw;
+                off = (((nb_ * p.Di + bd) * p.Hi + bh) * p.Wi + bw) * GC + g * p.C;
+            }
+            a_off[t] = off; a_bd[t] = bd; a_bh[t] = bh; a_bw[t] = bw;
+            ow += 8;
+            while (ow >= p.Wo) {
+                ow -= p.Wo;
+                if (++oh == p.Ho) {
+                    oh = 0;
+                    if (++od == p.Do) { od = 0; ++nb_; }
+                }
+            }
+        }
+    }
+    uint32_t b_off[S::B_PER_W];
+#pragma unroll
+    for (int t = 0; t < S::B_PER_W; ++t) {
+        const int n = n0 + (wave * S::B_PER_W + t) * 8 + lrow;
+        b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + chunk * S::VEC) * S::ESZ) : kOutOfRange;
+    }
+
+    // filter tap of reduction index r = k0 + chunk*VEC, stepped by one
+    // 128-byte sub-slice (SUBK elements) per call of issue_sub
+    int r = chunk * S::VEC;
+    int c, xk, yk, zk;
+    {
+        int tap = r / p.C;
+        c = r - tap * p.C;
+        xk = tap % p.X; tap /= p.X;
+        yk = tap % p.Y;
+        zk = tap / p.Y;
+    }
+
+    auto issue_sub = [&](uint32_t sub_base, int k0) {
+        const bool rok = r < p.Kred;
+        const int zd = zk * p.dd, yh = yk * p.dh, xw = xk * p.dw;
+        const int toff = ((zd * p.Hi + yh) * p.Wi + xw) * GC + c;
+        const uint32_t la = lds0 + sub_base + wave * S::A_PER_W * 1024;
+#pragma unroll
+        for (int t = 0; t < S::A_PER_W; ++t) {
+            const bool ok = rok && (unsigned)(a_bd[t] + zd) < (unsigned)p.Di &&
+                            (unsigned)(a_bh[t] + yh) < (unsigned)p.Hi &&
+                            (unsigned)(a_bw[t] + xw) < (unsigned)p.Wi;
+            dma16(xr, ok ? (uint32_t)((a_off[t] + toff) * S::ESZ) : kOutOfRange, 0, la + t * 1024);
+        }
+        const uint32_t lb = lds0 + sub_base + BM * 128 + wave * S::B_PER_W * 1024;
+#pragma unroll
+        for (int t = 0; t < S::B_PER_W; ++t)
+            dma16(wr, rok ? b_off[t] : kOutOfRange, (uint32_t)(k0 * S::ESZ), lb + t * 1024);
+        // advance to the next sub-slice
+        r += S::SUBK;
+        c += S::SUBK;
+        while (c >= p.C) {
+            c -= p.C;
+            if (++xk == p.X) {
+                xk = 0;
+                if (++yk == p.Y) { yk = 0; ++zk; }
+            }
+        }
+    };
+    auto issue = [&](int stage, int k0) {
+#pragma unroll
+        for (int u = 0; u < KSUB; ++u) issue_sub(stage * S::STAGE + u * S::SUB, k0 + u * S::SUBK);
+    };
+
+    AccT acc[S::MI][S::NI];
+#pragma unroll
+    for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+        for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+            for (int e = 0; e < S::ACC; ++e) acc[i][j][e] = 0.f;
+
+    // Operand rows: a 16x16 block feeds row (lane & 15) with the 16-byte
+    // chunk (lane >> 4) of each 64-byte half; a 32x32 block feeds row
+    // (lane & 31) with chunk (lane >> 5) of each 32-byte quarter.
+    const int frow = lane & (MF - 1);
+    const int fk = lane / MF;
+
+    // All fragments of a stage are read before any product is issued, so LDS
+    // latency is paid once per K-step.  The product is computed transposed
+    // (weights as the first operand), so each lane's results are runs of 4
+    // consecutive output channels of one pixel.
+    auto compute_sub = [&](const unsigned char *As) {
+        const unsigned char *Bs = As + BM * 128;
+        if constexpr (DT == 1 && MF == 32) {
+            // 32x32x16: four k sub-steps of 16 per 128-byte row; lane half fk
+            // takes chunk 2*q + fk
+            bf16x8_t a[4][S::MI], b[4][S::NI];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int sw = (((2 * q + fk) ^ (frow & 7)) << 4);
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+                    a[q][i] = *reinterpret_cast<const bf16x8_t *>(As + (wm * S::TM + i * 32 + frow) * 128 + sw);
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+                    b[q][j] = *reinterpret_cast<const bf16x8_t *>(Bs + (wn * S::TN + j * 32 + frow) * 128 + sw);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::NI; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q][j], a[q][i], acc[i][j], 0, 0, 0);
+        } else if constexpr (DT == 1) {
+            bf16x8_t a[2][S::MI], b[2][S::NI];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const int sw = (((kc * 4 + fk) ^ (frow & 7)) << 4);
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+                    a[kc][i] = *reinterpret_cast<const bf16x8_t *>(As + (wm * S::TM + i * 16 + frow) * 128 + sw);
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+                    b[kc][j] = *reinterpret_cast<const bf16x8_t *>(Bs + (wn * S::TN + j * 16 + frow) * 128 + sw);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::NI; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kc][j], a[kc][i], acc[i][j], 0, 0, 0);
+        } else {
+            // four 16x16x4 products over the 16 k of chunks kc*4 .. kc*4+3:
+            // lane group fk holds chunk kc*4+fk, product e uses its element e
+            f32x4_t a[2][S::MI], b[2][S::NI];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const int sw = (((kc * 4 + fk) ^ (frow & 7)) << 4);
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+                    a[kc][i] = *reinterpret_cast<const f32x4_t *>(As + (wm * S::TM + i * 16 + frow) * 128 + sw);
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+                    b[kc][j] = *reinterpret_cast<const f32x4_t *>(Bs + (wn * S::TN + j * 16 + frow) * 128 + sw);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                        for (int j = 0; j < S::NI; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[kc][j][e], a[kc][i][e], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    auto compute = [&](int stage) {
+#pragma unroll
+        for (int u = 0; u < KSUB; ++u) compute_sub(smem + stage * S::STAGE + u * S::SUB);
+    };
+
+    // ---- pipeline ---------------------------------------------------------
+    const int nk = (p.Kred + S::BK - 1) / S::BK;
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < nk) issue(s, s * S::BK);
+    for (int it = 0; it < nk; ++it) {
+        if (it + NS - 2 < nk) wait_vmcnt<S::L * (NS - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();                        // step it is in LDS for every wave
+        if (it + NS - 1 < nk) issue((it + NS - 1) % NS, (it + NS - 1) * S::BK);
+        compute(it % NS);
+    }
+    __syncthreads();
+
+    // ---- epilogue: bias, GELU, round, stage in LDS, whole-vector stores ---
+    // Transposed product: in a 16x16 block the lane holds channels
+    // 4*fk + e (e = 0..3) of pixel frow; in a 32x32 block it holds channels
+    // 8*h + 4*fk + e (h = 0..3, e = 0..3) of pixel frow.
+    constexpr int RUNS = S::ACC / 4;     // runs of 4 consecutive channels per block
+    T *Cs = reinterpret_cast<T *>(smem);
+#pragma unroll
+    for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+        for (int h = 0; h < RUNS; ++h) {
+            const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int n = n0 + nl + e;
+                    if (n < p.K) bv[e] = to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < S::MI; ++i) {
+                const int ml = wm * S::TM + i * MF + frow;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = acc[i][j][h * 4 + e] + bv[e];
+                    if constexpr (GELU) v[e] = gelu_erf(v[e]);
+                }
+                if constexpr (DT == 1) {
+                    uint2 pk;
+                    pk.x = f32x2_to_bf16x2(v[0], v[1]);
+                    pk.y = f32x2_to_bf16x2(v[2], v[3]);
+                    *reinterpret_cast<uint2 *>(Cs + ml * S::LDC + nl) = pk;
+                } else {
+                    *reinterpret_cast<f32x4_t *>(Cs + ml * S::LDC + nl) = f32x4_t{v[0], v[1], v[2], v[3]};
+                }
+            }
+        }
+    __syncthreads();
+
+    T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;
+    const int GK = p.G * p.K;
+    constexpr int OVPR = BN / S::VEC;
+    for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
+        const int row = idx / OVPR;
+        const int cv = idx % OVPR;
+        const int m = m0 + row;
+        const int n = n0 + cv * S::VEC;
+        if (m >= p.M || n >= p.K) continue;
+        const T *src = Cs + row * S::LDC + cv * S::VEC;
+        T *dst = yg + (size_t)m * GK + n;
+        if (p.out_vec) {
+            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+        } else {
+            const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
+            for (int e = 0; e < lim; ++e) dst[e] = src[e];
+        }
+    }
+}
+
+}  // namespace convfwd

@@ -68,13 +68,20 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h)
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// IEEE round-to-nearest-even float32 -> bfloat16 (NaN stays a quiet NaN).
+// IEEE round-to-nearest-even float32 -> bfloat16 (NaN stays NaN).  On
+// gfx950 the conversion is the hardware v_cvt_pk_bf16_f32, which rounds to
+// nearest-even in the default rounding mode.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two values at once: low half = a, high half = b.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float gelu_erf(float v)

@@ -1,0 +1,91 @@
+"""Times every eligible tile configuration on a grid of convolution problems
+through the C ABI and writes one CSV row per (problem, configuration).
+
+    python -m convolution_forward_implicit_amd.tuning.sweep OUT.csv
+
+Needs a GPU.  Timing: warm caches, 3 untimed launches, then the median of 15
+launches each bracketed by HIP events on the current stream.  Inputs are
+random (values do not affect the timing).
+"""
+import csv
+import itertools
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FIELDS = ["dtype", "N", "G", "C", "K", "Di", "Hi", "Wi", "Z", "Y", "X", "sd", "sh", "sw",
+          "pd", "ph", "pw", "dd", "dh", "dw", "config", "ms"]
+
+
+def problem(N, G, C, K, inp, filt, stride, pad, dil):
+    return {"N": N, "G": G, "C": C, "K": K, "in": tuple(inp), "filt": tuple(filt),
+            "stride": tuple(stride), "pad": tuple(pad), "dil": tuple(dil)}
+
+
+def grid():
+    """The calibration grid: audio-style 1-D convs (the Whisper frontend
+    shapes and neighbours), plain and grouped 2-D convs, grouped 3-D convs
+    with and without dilation."""
+    out = []
+    for N, C, K, L, k, s in [(1, 80, 384, 3000, 3, 1), (1, 384, 384, 3000, 3, 2), (4, 80, 384, 3000, 3, 1),
+                             (32, 80, 384, 3000, 3, 1), (32, 384, 384, 3000, 3, 2), (8, 256, 256, 1000, 3, 1),
+                             (1, 512, 512, 1500, 3, 1), (16, 128, 64, 2048, 5, 1), (2, 64, 128, 4096, 7, 2),
+                             (64, 384, 384, 500, 3, 1)]:
+        out.append(problem(N, 1, C, K, (1, 1, L), (1, 1, k), (1, 1, s), (0, 0, k // 2), (1, 1, 1)))
+    for N, G, C, K, H, k, s, p, d in [(8, 4, 64, 64, 56, 3, 1, 1, 1), (8, 1, 64, 64, 56, 3, 1, 1, 1),
+                                      (4, 1, 128, 128, 28, 3, 1, 1, 1), (16, 1, 256, 256, 14, 3, 1, 1, 1),
+                                      (8, 8, 32, 32, 56, 3, 1, 1, 1), (2, 32, 16, 16, 112, 3, 1, 1, 1),
+                                      (8, 1, 64, 128, 56, 1, 1, 0, 1), (4, 2, 128, 128, 28, 3, 2, 1, 1),
+                                      (8, 4, 64, 64, 56, 3, 1, 2, 2), (1, 1, 256, 256, 64, 3, 1, 1, 1),
+                                      (32, 1, 64, 64, 32, 3, 1, 1, 1), (8, 1, 512, 512, 7, 3, 1, 1, 1)]:
+        out.append(problem(N, G, C, K, (1, H, H), (1, k, k), (1, s, s), (0, p, p), (1, d, d)))
+    for N, G, C, K, D, H, k, p, d in [(2, 8, 32, 32, 16, 28, 3, 2, 2), (2, 1, 64, 64, 16, 28, 3, 1, 1),
+                                      (1, 4, 32, 32, 8, 56, 3, 1, 1), (4, 1, 32, 64, 8, 28, 3, 1, 1),
+                                      (2, 16, 16, 16, 16, 28, 3, 1, 1), (1, 2, 64, 64, 32, 32, 3, 1, 1)]:
+        out.append(problem(N, G, C, K, (D, H, H), (k, k, k), (1, 1, 1), (p, p, p), (d, d, d)))
+    return out
+
+
+def main(path):
+    import torch
+    from convolution_forward_implicit_amd import ConvFwd, ConvError, capi
+    dev = torch.device("cuda:0")
+    names = [capi.conv_fwd_config_name(i) for i in range(capi.conv_fwd_num_configs())]
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(FIELDS)
+        for p, dt in itertools.product(grid(), ["bf16", "f32"]):
+            if dt == "f32" and p["in"][1] > 1 and p["N"] > 4:
+                continue   # keep the fp32 part of the grid small
+            tdt = torch.float32 if dt == "f32" else torch.bfloat16
+            ref = ConvFwd(p, dt, True, False)
+            x = torch.randn(ref.x_shape, device=dev).to(tdt)
+            w = torch.randn(ref.w_shape, device=dev).to(tdt)
+            b = torch.randn(ref.b_shape, device=dev).to(tdt)
+            y = torch.empty(ref.y_shape, dtype=tdt, device=dev)
+            for ci, name in enumerate(names):
+                try:
+                    c = ConvFwd(p, dt, True, False, config=ci)
+                except ConvError:
+                    continue
+                for _ in range(3):
+                    c(x, w, b, out=y)
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(15)]
+                for a, e in evs:
+                    a.record()
+                    c(x, w, b, out=y)
+                    e.record()
+                torch.cuda.synchronize()
+                ts = sorted(a.elapsed_time(e) for a, e in evs)
+                wr.writerow([dt, p["N"], p["G"], p["C"], p["K"], *p["in"], *p["filt"], *p["stride"],
+                             *p["pad"], *p["dil"], name, "%.6f" % ts[len(ts) // 2]])
+            f.flush()
+            print("swept", dt, p, flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1] if len(sys.argv) > 1 else "sweep.csv")

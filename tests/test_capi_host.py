@@ -199,3 +199,29 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(capi, "LIB_PATH", str(tmp_path / "libconvfwd.so"))
     with pytest.raises(ImportError):
         capi.lib()
+
+
+def test_selector_coefficients_match_compiled_configs():
+    """Every fitted cost-model entry names a configuration the library
+    compiles (a stale coefficient table would silently fall back)."""
+    import os
+    inc = os.path.join(os.path.dirname(capi.LIB_PATH), "csrc", "selector_coef.inc")
+    names = {line.split('"')[1] for line in open(inc) if line.strip().startswith('{"')}
+    compiled = {capi.conv_fwd_config_name(i) for i in range(capi.conv_fwd_num_configs())}
+    assert names and names <= compiled, names - compiled
+    dma = {n for n in compiled if "_dma_" in n}
+    assert dma <= names, dma - names
+
+
+def test_selector_fit_reproduces_committed_table(tmp_path):
+    """tuning/fit.py applied to the committed sweep table regenerates the
+    committed coefficients, and its held-out selector quality is recorded."""
+    import os
+    from convolution_forward_implicit_amd.tuning import fit
+    here = os.path.dirname(capi.LIB_PATH)
+    probs = fit.load(os.path.join(here, "tuning", "sweep_mi355x.csv"))
+    out = tmp_path / "coef.inc"
+    fit.write(fit.fit(probs), str(out))
+    assert out.read_text() == open(os.path.join(here, "csrc", "selector_coef.inc")).read()
+    q = fit.quality(probs)
+    assert q["mean_eff"] > 0.9 and q["top5"] > 0.8, q
