@@ -13,10 +13,15 @@ grouped_conv3d_bf16_dil2.
 Prints ONE JSON line.  value = useful TFLOP/s of the whole step (2*MACs
 counting padded taps, over the wall time of K steps bracketed by device
 synchronisation).  roofline = the dominant (most flop) kernel: its useful
-flop per launch over its mean launch time, taken from HIP events recorded
-around each of its launches on the stream it runs on, against the MI355X
-dense MFMA peak of its dtype.  cpu_baseline = the fp64 oracle on the host
-cores over a bounded sample of the same workload.
+flop per launch over its mean duration, from HIP events that the launch
+itself records when the kernel starts and ends (on the stream it runs on),
+against the MI355X dense MFMA peak of its dtype.  cpu_baseline = the fp64
+oracle on the host cores over a bounded sample of the same workload.
+
+    python bench.py --copy-bytes B [--steps K]
+
+runs only a device-to-device copy of B bytes K times (the reference kernel
+that scales the FETCH_SIZE / WRITE_SIZE counters to bytes).
 """
 import argparse
 import hashlib
@@ -36,10 +41,13 @@ DEFAULT_WORKLOAD = "whisper_frontend_f32_b1"
 
 
 def kernel_source_hash():
+    """Hash of every source the HIP library is built from (kernels, host
+    code, selector coefficients)."""
     h = hashlib.sha256()
-    for rel in ("convolution_forward_implicit_amd/csrc/igemm_kernel.h",
-                "convolution_forward_implicit_amd/csrc/conv_fwd.hip"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
+    d = os.path.join(ROOT, "convolution_forward_implicit_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -60,8 +68,9 @@ def recorded_traffic(workload, layer_index, launches_bytes):
 
 def cpu_baseline(W, target_s):
     """Times the fp64 oracle on the host cores over a bounded sample of the
-    workload: whole layers when a layer is small, otherwise a random sample
-    of its outputs; the rate is useful flop of the sample over its time."""
+    workload: whole layers (repeated to fill the time budget) when a layer is
+    small, otherwise a random sample of its outputs; the rate is useful flop
+    of the sample over its time."""
     import numpy as np
     from oracle import ref
     flop, secs, parts = 0.0, 0.0, []
@@ -82,11 +91,14 @@ def cpu_baseline(W, target_s):
         t_cal = max(time.perf_counter() - t0, 1e-4)
         n = int(min(np.prod(ys), max(2000, 2000 * budget / t_cal)))
         if n >= np.prod(ys):
-            t0 = time.perf_counter()
-            y = ref.conv_fwd(p, xin, w, b, ge, want_absdot=False)
-            dt = time.perf_counter() - t0
-            parts.append("layer %d: all %d outputs" % (li + 1, int(np.prod(ys))))
-            flop += ref.useful_flop(p)
+            reps, dt = 0, 0.0
+            while reps == 0 or dt < budget:
+                t0 = time.perf_counter()
+                y = ref.conv_fwd(p, xin, w, b, ge, want_absdot=False)
+                dt += time.perf_counter() - t0
+                reps += 1
+            parts.append("layer %d: all %d outputs x %d" % (li + 1, int(np.prod(ys)), reps))
+            flop += ref.useful_flop(p) * reps
             x = y
         else:
             idx = rng.integers(0, int(np.prod(ys)), n)
@@ -109,6 +121,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a device copy of this many bytes --steps times")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -121,6 +135,15 @@ def main():
     import torch
     import synthdata as sd
     from convolution_forward_implicit_amd import ConvFwd
+
+    if args.copy_bytes:
+        a = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": a.numel() * 4, "launches": args.steps}), flush=True)
+        return
 
     W = sd.workload(args.workload)
     dt = W["dtype"]
@@ -145,11 +168,8 @@ def main():
     def step(ev=None, i=0):
         x = x0
         for li, c in enumerate(convs):
-            if ev is not None and li == dom:
-                ev[0][i].record(stream)
-            c(x, ws[li], bs[li], out=outs[li], stream=stream)
-            if ev is not None and li == dom:
-                ev[1][i].record(stream)
+            kev = (ev[0][i], ev[1][i]) if ev is not None and li == dom else None
+            c(x, ws[li], bs[li], out=outs[li], stream=stream, events=kev)
             x = outs[li]
 
     for _ in range(args.warmup):
@@ -159,6 +179,8 @@ def main():
     K = args.steps
     ev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
           [torch.cuda.Event(enable_timing=True) for _ in range(K)])
+    for e in ev[0] + ev[1]:
+        e.record(stream)              # creates the event handles the kernel launch records
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()

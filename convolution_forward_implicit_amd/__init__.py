@@ -89,7 +89,10 @@ class ConvFwd:
             raise ValueError("%s has %d elements, expected shape %r" % (name, t.numel(), shape))
         return t.data_ptr()
 
-    def __call__(self, x, w, bias=None, out=None, stream=None):
+    def __call__(self, x, w, bias=None, out=None, stream=None, events=None):
+        """events: optional (start, stop) torch.cuda.Event pair recorded when
+        the kernel itself starts and ends (each must have been recorded once,
+        so that its handle exists)."""
         import torch
         xp = self._tensor(x, self.x_shape, "x", torch)
         wp = self._tensor(w, self.w_shape, "w", torch)
@@ -104,5 +107,9 @@ class ConvFwd:
             out = torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
         yp = self._tensor(out, self.y_shape, "out", torch)
         s = stream if stream is not None else torch.cuda.current_stream(x.device)
-        capi.conv_fwd_run(self._plan, xp, wp, bp, yp, s.cuda_stream)
+        if events is None:
+            capi.conv_fwd_run(self._plan, xp, wp, bp, yp, s.cuda_stream)
+        else:
+            capi.conv_fwd_run_events(self._plan, xp, wp, bp, yp, s.cuda_stream,
+                                     events[0].cuda_event, events[1].cuda_event)
         return out

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTE
                 3: "CONV_ERR_HIP", 4: "CONV_ERR_NOMEM"}
 
 EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims",
-            "conv_fwd_run", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
+            "conv_fwd_run", "conv_fwd_run_events", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
             "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error"]
 
 
@@ -67,6 +67,8 @@ def lib():
         L.conv_fwd_out_dims.restype = ctypes.c_int
         L.conv_fwd_run.argtypes = [P, P, P, P, P, P]
         L.conv_fwd_run.restype = ctypes.c_int
+        L.conv_fwd_run_events.argtypes = [P, P, P, P, P, P, P, P]
+        L.conv_fwd_run_events.restype = ctypes.c_int
         L.conv_fwd_destroy.argtypes = [P]
         L.conv_fwd_destroy.restype = None
         L.conv_fwd_describe.argtypes = [P]
@@ -122,6 +124,10 @@ def conv_fwd_out_dims(plan):
 
 def conv_fwd_run(plan, x, w, bias, y, stream=0):
     _check(lib().conv_fwd_run(plan, x, w, bias, y, stream))
+
+
+def conv_fwd_run_events(plan, x, w, bias, y, stream=0, start_event=None, stop_event=None):
+    _check(lib().conv_fwd_run_events(plan, x, w, bias, y, stream, start_event, stop_event))
 
 
 def conv_fwd_destroy(plan):

@@ -10,6 +10,7 @@
 // (section 1: choosing among tile/pipeline variants per dim tuple), and like
 // the onnxruntime subgroup-matrix MatMul change it prefers big tiles for big
 // problems and smaller ones where big tiles would leave compute units idle.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,19 +39,23 @@ conv_status_t fail(conv_status_t st, const char *fmt, ...)
     return st;
 }
 
-typedef void (*launch_fn)(const KParams &, uint32_t x_bytes, uint32_t w_bytes, int grid, hipStream_t);
+typedef void (*launch_fn)(const KParams &, uint32_t x_bytes, uint32_t w_bytes, int grid, hipStream_t,
+                          hipEvent_t start, hipEvent_t stop);
 
+// hipExtLaunchKernelGGL records the optional events when the kernel itself
+// starts and ends.
 template <int DT, int BM, int BN, int BK, int WM, int WN, int VEC>
-void launch_reg(const KParams &kp, uint32_t, uint32_t, int grid, hipStream_t s)
+void launch_reg(const KParams &kp, uint32_t, uint32_t, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 {
-    hipLaunchKernelGGL((igemm_fwd_kernel<DT, BM, BN, BK, WM, WN, VEC>), dim3(grid),
-                       dim3(WM * WN * 64), 0, s, kp);
+    hipExtLaunchKernelGGL((igemm_fwd_kernel<DT, BM, BN, BK, WM, WN, VEC>), dim3(grid),
+                          dim3(WM * WN * 64), 0, s, e0, e1, 0, kp);
 }
 
 // The epilogue (bias, GELU) is compiled into each kernel variant, so a
 // variant carries only the code it runs.
 template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB>
-void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s)
+void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
+                hipEvent_t e1)
 {
     DmaParams dp;
     dp.k = kp;
@@ -59,13 +64,13 @@ void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream
     const dim3 g(grid), b(WM * WN * 64);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
-        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, true>), g, b, 0, s, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, true>), g, b, 0, s, e0, e1, 0, dp);
     else if (bias)
-        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, false>), g, b, 0, s, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, false>), g, b, 0, s, e0, e1, 0, dp);
     else if (kp.gelu)
-        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, true>), g, b, 0, s, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, true>), g, b, 0, s, e0, e1, 0, dp);
     else
-        hipLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, false>), g, b, 0, s, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, false>), g, b, 0, s, e0, e1, 0, dp);
 }
 
 struct TileCfg {
@@ -402,8 +407,9 @@ static bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
     return pa < pb + bn && pb < pa + an;
 }
 
-conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const void *w,
-                           const void *bias, void *y, void *stream)
+conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, const void *w,
+                                  const void *bias, void *y, void *stream, void *start_event,
+                                  void *stop_event)
 {
     if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
     const conv_fwd_desc_t &d = plan->desc;
@@ -425,10 +431,16 @@ conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const voi
     (void)d;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     kCfgs[plan->cfg].fn(kp, (uint32_t)(plan->x_elems * e), (uint32_t)(plan->w_elems * e), plan->grid,
-                        (hipStream_t)stream);
+                        (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return CONV_OK;
+}
+
+conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const void *w,
+                           const void *bias, void *y, void *stream)
+{
+    return conv_fwd_run_events(plan, x, w, bias, y, stream, nullptr, nullptr);
 }
 
 void conv_fwd_destroy(conv_fwd_plan_t *plan) { delete plan; }

@@ -125,17 +125,19 @@ igemm_dma_kernel(DmaParams dp)
     const int wm = wave / WN;
     const int wn = wave % WN;
 
-    // Workgroups are handed to the 8 XCDs round-robin; give each XCD a
-    // contiguous run of tiles so neighbouring output rows (which share input
-    // halo rows) meet in the same L2.
+    // Workgroups are handed to the 8 XCDs round-robin.  Renumber them so each
+    // XCD gets a contiguous run of tiles, and order tiles output-channel
+    // fastest: an XCD then covers a slab of output rows with all their
+    // channel tiles, so each input row is fetched into one XCD's L2 only and
+    // only the (small) weight tensor is replicated across XCDs.
     const int nb = gridDim.x;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = nb >> 3, rem = nb & 7;
     int bid = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    const int m_tile = bid % p.tiles_m;
-    bid /= p.tiles_m;
     const int n_tile = bid % p.tiles_n;
-    const int g = bid / p.tiles_n;
+    bid /= p.tiles_n;
+    const int m_tile = bid % p.tiles_m;
+    const int g = bid / p.tiles_m;
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
 

@@ -115,6 +115,15 @@ conv_status_t conv_fwd_out_dims(const conv_fwd_plan_t *plan, int64_t out[3]);
 conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const void *w,
                            const void *bias, void *y, void *stream);
 
+/* As conv_fwd_run, and additionally records start_event when the kernel
+ * starts executing and stop_event when it ends (hipEvent_t handles created
+ * by the caller, either may be NULL), so hipEventElapsedTime gives the
+ * kernel's own duration without the launch gap before it.  For measuring the
+ * kernels' throughput; errors as conv_fwd_run. */
+conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, const void *w,
+                                  const void *bias, void *y, void *stream,
+                                  void *start_event, void *stop_event);
+
 /* Frees a plan.  NULL is a no-op. */
 void conv_fwd_destroy(conv_fwd_plan_t *plan);
 
