@@ -24,6 +24,7 @@
 #include "../../include/convfwd.h"
 #include "igemm_kernel.h"
 #include "igemm_dma.h"
+#include "patch_kernel.h"
 
 namespace convfwd {
 namespace {
@@ -73,33 +74,83 @@ void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream
         hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, false>), g, b, 0, s, e0, e1, 0, dp);
 }
 
+FastDiv make_fastdiv(int d);
+
+template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX>
+void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
+                  hipEvent_t e1)
+{
+    PatchParams pp;
+    pp.k = kp;
+    pp.x_bytes = xb;
+    pp.w_bytes = wb;
+    pp.tiles_h = (kp.Ho + TH - 1) / TH;
+    pp.tiles_w = (kp.Wo + TW - 1) / TW;
+    pp.ph = (TH - 1) * kp.sh + (kp.Y - 1) * kp.dh + 1;
+    pp.pw = (TW - 1) * kp.sw + (kp.X - 1) * kp.dw + 1;
+    pp.fd_pw = make_fastdiv(pp.pw);
+    pp.fd_taps = make_fastdiv(kp.Y * kp.X);
+    const dim3 g(grid), b(256);
+    const bool bias = kp.bias != nullptr;
+    if (bias && kp.gelu)
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, true, true>), g, b, 0, s, e0, e1, 0, pp);
+    else if (bias)
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, true, false>), g, b, 0, s, e0, e1, 0, pp);
+    else if (kp.gelu)
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, false, true>), g, b, 0, s, e0, e1, 0, pp);
+    else
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, false, false>), g, b, 0, s, e0, e1, 0, pp);
+}
+
+enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2 };
+
 struct TileCfg {
     int dtype;          // conv_dtype_t
-    int dma;            // 1: direct global->LDS pipeline, 0: register-staged
+    int kind;           // KIND_REG: register-staged implicit GEMM, KIND_DMA: direct-to-LDS
+                        // implicit GEMM, KIND_PATCH: input patch in LDS
     int BM, BN, BK, WM, WN, VEC, NS;
     int lds_bytes;
     launch_fn fn;
     const char *name;
+    int TH, TW, CC, PHMAX, PWMAX, TAPMAX;   // KIND_PATCH only
 };
 
 #define CFG(DT, BM, BN, BK, WM, WN, VEC)                                                 \
-    TileCfg{DT, 0, BM, BN, BK, WM, WN, VEC, 2,                                           \
+    TileCfg{DT, KIND_REG, BM, BN, BK, WM, WN, VEC, 2,                                    \
             IgemmShape<DT, BM, BN, BK, WM, WN, VEC>::LDS_BYTES,                          \
             &launch_reg<DT, BM, BN, BK, WM, WN, VEC>,                                    \
             (DT ? "bf16_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC                 \
-                : "f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC)}
+                : "f32_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_v" #VEC),                \
+            0, 0, 0, 0, 0, 0}
 
 #define DMA(DT, BM, BN, WM, WN, NS, MF, KSUB)                                            \
-    TileCfg{DT, 1, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS,     \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
             DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB>::LDS_BYTES,                        \
             &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB>,                               \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB  \
-                : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB)}
+                : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB), \
+            0, 0, 0, 0, 0, 0}
+
+// Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
+// CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
+// filter taps per depth tap.
+#define PATCH(TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX)                                  \
+    TileCfg{1, KIND_PATCH, TH * TW, BN, CC, 4, 1, 8, NS,                                  \
+            PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX>::LDS_BYTES,              \
+            &launch_patch<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX>,                     \
+            "bf16_patch_" #TH "x" #TW "x" #BN "_c" #CC "_s" #NS "_p" #PHMAX "x" #PWMAX,   \
+            TH, TW, CC, PHMAX, PWMAX, TAPMAX}
 
 // One candidate table, shared by the selector, forced-config creation and
 // the sweeps.  VEC = 16 bytes of channels per load; the VEC = 1 entries serve
 // channel counts that are not a multiple of the vector.
 const TileCfg kCfgs[] = {
+    PATCH(8, 32, 64, 16, 2, 10, 34, 9),
+    PATCH(4, 32, 64, 16, 2, 6, 34, 9),
+    PATCH(8, 32, 32, 16, 2, 12, 36, 9),
+    PATCH(4, 32, 32, 16, 2, 8, 36, 9),
+    PATCH(8, 32, 64, 32, 2, 10, 34, 9),
+    PATCH(8, 16, 64, 16, 2, 10, 18, 9),
     DMA(1, 128, 128, 2, 2, 2, 32, 1),
     DMA(1, 128, 128, 2, 2, 2, 32, 2),
     DMA(1, 256, 64, 4, 1, 2, 32, 1),
@@ -112,9 +163,15 @@ const TileCfg kCfgs[] = {
     DMA(1, 128, 32, 4, 1, 2, 16, 1),
     DMA(1, 128, 32, 4, 1, 2, 16, 2),
     DMA(1, 64, 32, 2, 2, 2, 16, 2),
+    DMA(1, 128, 64, 2, 2, 3, 16, 1),
+    DMA(1, 128, 32, 4, 1, 3, 16, 1),
+    DMA(1, 64, 64, 2, 2, 3, 16, 1),
+    DMA(1, 128, 128, 2, 2, 3, 32, 1),
     DMA(0, 32, 32, 2, 2, 2, 16, 1),
     DMA(0, 32, 32, 2, 2, 2, 16, 2),
     DMA(0, 32, 32, 2, 2, 2, 16, 4),
+    DMA(0, 32, 32, 2, 2, 3, 16, 2),
+    DMA(0, 32, 32, 2, 2, 4, 16, 2),
     DMA(0, 32, 64, 1, 4, 2, 16, 1),
     DMA(0, 32, 64, 1, 4, 2, 16, 2),
     DMA(0, 64, 32, 4, 1, 2, 16, 2),
@@ -138,11 +195,11 @@ constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
 
 // Per-configuration cost coefficients fitted to a sweep of every
 // configuration over a grid of problems (tuning/fit.py): predicted
-// milliseconds t = a + b*r + d*r*nk, r = workgroups per compute unit, nk =
-// K-steps per workgroup.
+// milliseconds t = a + b*r + d*r*nk + e*nk, r = workgroups per compute unit,
+// nk = K-steps per workgroup.
 struct CostCoef {
     const char *name;
-    double a, b, d;
+    double a, b, d, e;
 };
 const CostCoef kCoef[] = {
 #include "selector_coef.inc"
@@ -153,6 +210,17 @@ const CostCoef *coef_of(const TileCfg &c)
     for (const CostCoef &k : kCoef)
         if (strcmp(k.name, c.name) == 0) return &k;
     return nullptr;
+}
+
+FastDiv make_fastdiv(int d)
+{
+    FastDiv f;
+    uint32_t s = 0;
+    while ((1ull << s) < (uint64_t)d) ++s;
+    f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << s) - (uint64_t)d)) / (uint64_t)d + 1);
+    f.s = s;
+    f.d = (uint32_t)d;
+    return f;
 }
 
 int device_cu_count()
@@ -254,7 +322,7 @@ double cost(const TileCfg &c, const conv_fwd_plan &pl, int cus)
     const double intensity = tmw * tnw / (tmw + tnw);                          // 8 .. 43
     double eff = std::min(1.0, intensity / (d.dtype == CONV_DT_BF16 ? 40.0 : 12.0));
     eff *= (double)(c.WM * c.WN) / 4.0;                                          // waves per CU
-    if (c.dma) eff = std::min(1.0, eff * 2.0);                                   // no register staging
+    if (c.kind != KIND_REG) eff = std::min(1.0, eff * 2.0);                      // no register staging
     const double rounds = std::ceil(tiles / cus);
     const double t_mfma = rounds * flop_tile / (cu_rate * std::max(eff, 0.05));
     const double bytes = (double)pl.esz * (pl.x_elems + pl.w_elems + pl.b_elems + pl.y_elems);
@@ -262,18 +330,40 @@ double cost(const TileCfg &c, const conv_fwd_plan &pl, int cus)
     return std::max(t_mfma, t_mem) + 1e-7 * kpad / c.BK;  // small per-step overhead
 }
 
+// Workgroups of a configuration on a problem, and K-steps per workgroup.
+double tiles_of(const TileCfg &c, const conv_fwd_desc_t &d, const int64_t out[3])
+{
+    const double tn = (double)((d.K + c.BN - 1) / c.BN);
+    if (c.kind == KIND_PATCH)
+        return (double)d.N * out[0] * (double)((out[1] + c.TH - 1) / c.TH) *
+               (double)((out[2] + c.TW - 1) / c.TW) * tn * (double)d.G;
+    const int64_t M = d.N * out[0] * out[1] * out[2];
+    return (double)((M + c.BM - 1) / c.BM) * tn * (double)d.G;
+}
+
+double steps_of(const TileCfg &c, const conv_fwd_desc_t &d)
+{
+    if (c.kind == KIND_PATCH) return (double)d.filt[0] * (double)(d.C / c.CC);
+    const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
+    return (double)((Kred + c.BK - 1) / c.BK);
+}
+
 // Predicted milliseconds of one configuration on the plan's problem.
 double predicted_ms(const TileCfg &c, const conv_fwd_plan &pl, int cus)
 {
     const CostCoef *k = coef_of(c);
     if (!k) return 1e3 * cost(c, pl, cus) * 10.0;   // uncalibrated: last resort
-    const conv_fwd_desc_t &d = pl.desc;
-    const int64_t M = d.N * pl.out[0] * pl.out[1] * pl.out[2];
-    const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
-    const double tiles = (double)((M + c.BM - 1) / c.BM) * (double)((d.K + c.BN - 1) / c.BN) * (double)d.G;
-    const double r = std::ceil(tiles / cus);
-    const double nk = (double)((Kred + c.BK - 1) / c.BK);
-    return k->a + k->b * r + k->d * r * nk;
+    const double r = std::ceil(tiles_of(c, pl.desc, pl.out) / cus);
+    const double nk = steps_of(c, pl.desc);
+    return k->a + k->b * r + k->d * r * nk + k->e * nk;
+}
+
+// The patch kernel's shape limits: channel slices, patch extent, taps.
+bool patch_fits(const TileCfg &c, const conv_fwd_desc_t &d)
+{
+    const int64_t ph = (c.TH - 1) * d.stride[1] + (d.filt[1] - 1) * d.dilation[1] + 1;
+    const int64_t pw = (c.TW - 1) * d.stride[2] + (d.filt[2] - 1) * d.dilation[2] + 1;
+    return d.C % c.CC == 0 && ph <= c.PHMAX && pw <= c.PWMAX && d.filt[1] * d.filt[2] <= c.TAPMAX;
 }
 
 }  // namespace
@@ -319,7 +409,10 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     const bool dma_ok = want_vec == vec && pl->x_elems * pl->esz < (int64_t(1) << 31) &&
                         pl->w_elems * pl->esz < (int64_t(1) << 31);
     auto eligible = [&](const TileCfg &c) {
-        return c.dtype == d.dtype && (c.dma ? dma_ok : c.VEC == want_vec);
+        if (c.dtype != d.dtype) return false;
+        if (c.kind == KIND_REG) return c.VEC == want_vec;
+        if (c.kind == KIND_DMA) return dma_ok;
+        return dma_ok && patch_fits(c, d);
     };
     if (forced >= 0) {
         if (forced >= kNumCfgs) {
@@ -333,8 +426,10 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         }
         if (c.VEC != 1 && !eligible(c)) {
             delete pl;
-            return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)%s", c.name, c.VEC,
-                        (long long)d.C, c.dma ? " and x, w below 2 GiB" : "");
+            return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)%s", c.name,
+                        c.kind == KIND_PATCH ? c.CC : c.VEC, (long long)d.C,
+                        c.kind == KIND_PATCH ? ", x and w below 2 GiB, and a patch / tap count within its limits"
+                        : c.kind == KIND_DMA ? " and x, w below 2 GiB" : "");
         }
         pl->cfg = forced;
     } else {
@@ -364,16 +459,28 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     kp.tiles_n = (kp.K + c.BN - 1) / c.BN;
     kp.gelu = d.gelu;
     kp.out_vec = (d.K % (16 / pl->esz) == 0) ? 1 : 0;
-    const double grid = (double)kp.tiles_m * kp.tiles_n * d.G;
+    kp.fd_Wo = make_fastdiv(kp.Wo);
+    kp.fd_Ho = make_fastdiv(kp.Ho);
+    kp.fd_Do = make_fastdiv(kp.Do);
+    kp.fd_C = make_fastdiv(kp.C);
+    kp.fd_X = make_fastdiv(kp.X);
+    kp.fd_Y = make_fastdiv(kp.Y);
+    const double grid = tiles_of(c, d, out);
     if (grid >= 2147483647.0) {
         delete pl;
         return fail(CONV_ERR_UNSUPPORTED, "grid too large");
     }
     pl->grid = (int)grid;
-    snprintf(pl->text, sizeof(pl->text),
-             "igemm %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%dx%d tiles) lds=%dB%s",
-             c.name, kp.M, kp.K, kp.Kred, kp.G, pl->grid, kp.tiles_m, kp.tiles_n, kp.G, c.lds_bytes,
-             forced >= 0 ? " forced" : "");
+    if (c.kind == KIND_PATCH)
+        snprintf(pl->text, sizeof(pl->text),
+                 "patch %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%d boxes/plane, %d n-tiles) lds=%dB%s", c.name,
+                 kp.M, kp.K, kp.Kred, kp.G, pl->grid, (kp.Ho + c.TH - 1) / c.TH, (kp.Wo + c.TW - 1) / c.TW,
+                 kp.tiles_n, c.lds_bytes, forced >= 0 ? " forced" : "");
+    else
+        snprintf(pl->text, sizeof(pl->text),
+                 "igemm %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%dx%d tiles) lds=%dB%s",
+                 c.name, kp.M, kp.K, kp.Kred, kp.G, pl->grid, kp.tiles_m, kp.tiles_n, kp.G, c.lds_bytes,
+                 forced >= 0 ? " forced" : "");
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
     return CONV_OK;

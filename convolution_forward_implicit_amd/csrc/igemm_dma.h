@@ -154,11 +154,12 @@ igemm_dma_kernel(DmaParams dp)
     int a_off[S::A_PER_W], a_bd[S::A_PER_W], a_bh[S::A_PER_W], a_bw[S::A_PER_W];
     {
         const int mfirst = m0 + wave * S::A_PER_W * 8 + lrow;
-        int q = mfirst;
-        int ow = q % p.Wo; q /= p.Wo;
-        int oh = q % p.Ho; q /= p.Ho;
-        int od = q % p.Do;
-        int nb_ = q / p.Do;
+        int q = fdiv(mfirst, p.fd_Wo);
+        int ow = mfirst - q * p.Wo;
+        int q2 = fdiv(q, p.fd_Ho);
+        int oh = q - q2 * p.Ho;
+        int nb_ = fdiv(q2, p.fd_Do);
+        int od = q2 - nb_ * p.Do;
 #pragma unroll
         for (int t = 0; t < S::A_PER_W; ++t) {
             const int m = mfirst + t * 8;
@@ -192,43 +193,56 @@ igemm_dma_kernel(DmaParams dp)
     int r = chunk * S::VEC;
     int c, xk, yk, zk;
     {
-        int tap = r / p.C;
+        const int tap = fdiv(r, p.fd_C);
         c = r - tap * p.C;
-        xk = tap % p.X; tap /= p.X;
-        yk = tap % p.Y;
-        zk = tap / p.Y;
+        const int t2 = fdiv(tap, p.fd_X);
+        xk = tap - t2 * p.X;
+        zk = fdiv(t2, p.fd_Y);
+        yk = t2 - zk * p.Y;
     }
 
-    auto issue_sub = [&](uint32_t sub_base, int k0) {
-        const bool rok = r < p.Kred;
-        const int zd = zk * p.dd, yh = yk * p.dh, xw = xk * p.dw;
-        const int toff = ((zd * p.Hi + yh) * p.Wi + xw) * GC + c;
-        const uint32_t la = lds0 + sub_base + wave * S::A_PER_W * 1024;
+    // DMA offsets of one stage, computed ahead (prep) and issued one at a
+    // time between the MFMAs of the previous stage (fire), so the loads'
+    // address arithmetic and issue run in the shadow of the matrix core.
+    constexpr int LPS = S::A_PER_W + S::B_PER_W;   // loads per wave and sub-slice
+    uint32_t dv[KSUB][LPS];
+    auto prep = [&](int k0) {
 #pragma unroll
-        for (int t = 0; t < S::A_PER_W; ++t) {
-            const bool ok = rok && (unsigned)(a_bd[t] + zd) < (unsigned)p.Di &&
-                            (unsigned)(a_bh[t] + yh) < (unsigned)p.Hi &&
-                            (unsigned)(a_bw[t] + xw) < (unsigned)p.Wi;
-            dma16(xr, ok ? (uint32_t)((a_off[t] + toff) * S::ESZ) : kOutOfRange, 0, la + t * 1024);
-        }
-        const uint32_t lb = lds0 + sub_base + BM * 128 + wave * S::B_PER_W * 1024;
+        for (int u = 0; u < KSUB; ++u) {
+            const bool rok = r < p.Kred;
+            const int zd = zk * p.dd, yh = yk * p.dh, xw = xk * p.dw;
+            const int toff = ((zd * p.Hi + yh) * p.Wi + xw) * GC + c;
 #pragma unroll
-        for (int t = 0; t < S::B_PER_W; ++t)
-            dma16(wr, rok ? b_off[t] : kOutOfRange, (uint32_t)(k0 * S::ESZ), lb + t * 1024);
-        // advance to the next sub-slice
-        r += S::SUBK;
-        c += S::SUBK;
-        while (c >= p.C) {
-            c -= p.C;
-            if (++xk == p.X) {
-                xk = 0;
-                if (++yk == p.Y) { yk = 0; ++zk; }
+            for (int t = 0; t < S::A_PER_W; ++t) {
+                const bool ok = rok && (unsigned)(a_bd[t] + zd) < (unsigned)p.Di &&
+                                (unsigned)(a_bh[t] + yh) < (unsigned)p.Hi &&
+                                (unsigned)(a_bw[t] + xw) < (unsigned)p.Wi;
+                dv[u][t] = ok ? (uint32_t)((a_off[t] + toff) * S::ESZ) : kOutOfRange;
+            }
+            const uint32_t kb = (uint32_t)((k0 + u * S::SUBK) * S::ESZ);
+#pragma unroll
+            for (int t = 0; t < S::B_PER_W; ++t)
+                dv[u][S::A_PER_W + t] = (rok && b_off[t] != kOutOfRange) ? b_off[t] + kb : kOutOfRange;
+            // advance to the next sub-slice
+            r += S::SUBK;
+            c += S::SUBK;
+            while (c >= p.C) {
+                c -= p.C;
+                if (++xk == p.X) {
+                    xk = 0;
+                    if (++yk == p.Y) { yk = 0; ++zk; }
+                }
             }
         }
     };
-    auto issue = [&](int stage, int k0) {
-#pragma unroll
-        for (int u = 0; u < KSUB; ++u) issue_sub(stage * S::STAGE + u * S::SUB, k0 + u * S::SUBK);
+    // load number q (0 .. L-1) of the prepared stage into LDS stage `stage`
+    auto fire = [&](int stage, int q) {
+        const int u = q / LPS, t = q % LPS;
+        const uint32_t base = lds0 + stage * S::STAGE + u * S::SUB;
+        if (t < S::A_PER_W)
+            dma16(xr, dv[u][t], 0, base + (wave * S::A_PER_W + t) * 1024);
+        else
+            dma16(wr, dv[u][t], 0, base + BM * 128 + (wave * S::B_PER_W + (t - S::A_PER_W)) * 1024);
     };
 
     AccT acc[S::MI][S::NI];
@@ -245,97 +259,78 @@ igemm_dma_kernel(DmaParams dp)
     const int frow = lane & (MF - 1);
     const int fk = lane / MF;
 
-    // All fragments of a stage are read before any product is issued, so LDS
-    // latency is paid once per K-step.  The product is computed transposed
-    // (weights as the first operand), so each lane's results are runs of 4
-    // consecutive output channels of one pixel.
-    auto compute_sub = [&](const unsigned char *As) {
-        const unsigned char *Bs = As + BM * 128;
-        if constexpr (DT == 1 && MF == 32) {
-            // 32x32x16: four k sub-steps of 16 per 128-byte row; lane half fk
-            // takes chunk 2*q + fk
-            bf16x8_t a[4][S::MI], b[4][S::NI];
+    // One stage: per sub-slice, all fragments are read first (one LDS
+    // latency per sub-slice), then the products run; the prepared loads of
+    // the stage `dst` (if >= 0) are spread between the products.  The
+    // product is transposed (weights as the first operand), so each lane's
+    // results are runs of 4 consecutive output channels.
+    constexpr int QS = (DT == 1 && MF == 32) ? 4 : 2;              // fragment reads per 128-byte row
+    constexpr int EPQ = (DT == 1) ? 1 : 4;                         // products per fragment pair
+    constexpr int NMF = KSUB * QS * EPQ * S::MI * S::NI;           // products per stage
+    auto compute = [&](int stage, int dst) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int sw = (((2 * q + fk) ^ (frow & 7)) << 4);
+        for (int u = 0; u < KSUB; ++u) {
+            const unsigned char *As = smem + stage * S::STAGE + u * S::SUB;
+            const unsigned char *Bs = As + BM * 128;
+            typedef typename std::conditional<DT == 1, bf16x8_t, f32x4_t>::type Frag;
+            Frag a[QS][S::MI], b[QS][S::NI];
+#pragma unroll
+            for (int q = 0; q < QS; ++q) {
+                // 32x32 blocks: lane half fk takes chunk 2q+fk; 16x16 blocks:
+                // lane quarter fk takes chunk 4q+fk
+                const int ch = (MF == 32 && DT == 1) ? 2 * q + fk : 4 * q + fk;
+                const int sw = ((ch ^ (frow & 7)) << 4);
 #pragma unroll
                 for (int i = 0; i < S::MI; ++i)
-                    a[q][i] = *reinterpret_cast<const bf16x8_t *>(As + (wm * S::TM + i * 32 + frow) * 128 + sw);
+                    a[q][i] = *reinterpret_cast<const Frag *>(As + (wm * S::TM + i * MF + frow) * 128 + sw);
 #pragma unroll
                 for (int j = 0; j < S::NI; ++j)
-                    b[q][j] = *reinterpret_cast<const bf16x8_t *>(Bs + (wn * S::TN + j * 32 + frow) * 128 + sw);
+                    b[q][j] = *reinterpret_cast<const Frag *>(Bs + (wn * S::TN + j * MF + frow) * 128 + sw);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < QS; ++q)
 #pragma unroll
-                for (int i = 0; i < S::MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < S::NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q][j], a[q][i], acc[i][j], 0, 0, 0);
-        } else if constexpr (DT == 1) {
-            bf16x8_t a[2][S::MI], b[2][S::NI];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const int sw = (((kc * 4 + fk) ^ (frow & 7)) << 4);
-#pragma unroll
-                for (int i = 0; i < S::MI; ++i)
-                    a[kc][i] = *reinterpret_cast<const bf16x8_t *>(As + (wm * S::TM + i * 16 + frow) * 128 + sw);
-#pragma unroll
-                for (int j = 0; j < S::NI; ++j)
-                    b[kc][j] = *reinterpret_cast<const bf16x8_t *>(Bs + (wn * S::TN + j * 16 + frow) * 128 + sw);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int i = 0; i < S::MI; ++i)
-#pragma unroll
-                    for (int j = 0; j < S::NI; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[kc][j], a[kc][i], acc[i][j], 0, 0, 0);
-        } else {
-            // four 16x16x4 products over the 16 k of chunks kc*4 .. kc*4+3:
-            // lane group fk holds chunk kc*4+fk, product e uses its element e
-            f32x4_t a[2][S::MI], b[2][S::NI];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                const int sw = (((kc * 4 + fk) ^ (frow & 7)) << 4);
-#pragma unroll
-                for (int i = 0; i < S::MI; ++i)
-                    a[kc][i] = *reinterpret_cast<const f32x4_t *>(As + (wm * S::TM + i * 16 + frow) * 128 + sw);
-#pragma unroll
-                for (int j = 0; j < S::NI; ++j)
-                    b[kc][j] = *reinterpret_cast<const f32x4_t *>(Bs + (wn * S::TN + j * 16 + frow) * 128 + sw);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < EPQ; ++e)
 #pragma unroll
                     for (int i = 0; i < S::MI; ++i)
 #pragma unroll
-                        for (int j = 0; j < S::NI; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[kc][j][e], a[kc][i][e], acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < S::NI; ++j) {
+                            if constexpr (DT == 1 && MF == 32)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q][j], a[q][i], acc[i][j], 0, 0, 0);
+                            else if constexpr (DT == 1)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[q][j], a[q][i], acc[i][j], 0, 0, 0);
+                            else
+                                // four 16x16x4 products over the 16 k of chunks 4q .. 4q+3: lane
+                                // quarter fk holds chunk 4q+fk, product e uses its element e
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q][j][e], a[q][i][e], acc[i][j], 0, 0, 0);
+                            const int m = (((u * QS + q) * EPQ + e) * S::MI + i) * S::NI + j;
+                            const int q0 = m * S::L / NMF, q1 = (m + 1) * S::L / NMF;
+                            if (dst >= 0) {
+#pragma unroll
+                                for (int qq = q0; qq < q1; ++qq) fire(dst, qq);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
         }
     };
 
-    auto compute = [&](int stage) {
-#pragma unroll
-        for (int u = 0; u < KSUB; ++u) compute_sub(smem + stage * S::STAGE + u * S::SUB);
-    };
-
-    // ---- pipeline ---------------------------------------------------------
+    // ---- pipeline: stage it+NS-1 is loaded while stage it is multiplied ---
     const int nk = (p.Kred + S::BK - 1) / S::BK;
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) issue(s, s * S::BK);
+        if (s < nk) {
+            prep(s * S::BK);
+#pragma unroll
+            for (int q = 0; q < S::L; ++q) fire(s, q);
+        }
     for (int it = 0; it < nk; ++it) {
         if (it + NS - 2 < nk) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();                        // step it is in LDS for every wave
-        if (it + NS - 1 < nk) issue((it + NS - 1) % NS, (it + NS - 1) * S::BK);
-        compute(it % NS);
+        const bool more = it + NS - 1 < nk;     // the buffer it refills was read in step it-1
+        if (more) prep((it + NS - 1) * S::BK);
+        compute(it % NS, more ? (it + NS - 1) % NS : -1);
     }
     __syncthreads();
 

@@ -34,6 +34,19 @@ namespace convfwd {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
+// Division by a divisor fixed at plan time: n / d = (umulhi(n, m) + n) >> s
+// for 0 <= n < 2^31, with s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994).  The host fills m and s.
+struct FastDiv {
+    uint32_t m, s, d;
+};
+
+__device__ __forceinline__ int fdiv(int n, FastDiv f)
+{
+    return (int)((__umulhi((uint32_t)n, f.m) + (uint32_t)n) >> f.s);
+}
+
 struct KParams {
     const void *x;
     const void *w;
@@ -52,6 +65,7 @@ struct KParams {
     int tiles_n;        // ceil(K / BN)
     int gelu;
     int out_vec;        // K % (16 / sizeof(out)) == 0: whole-vector stores
+    FastDiv fd_Wo, fd_Ho, fd_Do, fd_C, fd_X, fd_Y;
 };
 
 template <int BYTES> struct RawVec;

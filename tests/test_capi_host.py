@@ -43,7 +43,7 @@ def test_out_dims_match_oracle_at_every_workload(wid):
         plan = capi.conv_fwd_create(desc_from_problem(p, sd.dtype_of(wid), hb, ge))
         try:
             assert capi.conv_fwd_out_dims(plan) == ref.out_dims(p)
-            assert "igemm" in capi.conv_fwd_describe(plan)
+            assert capi.conv_fwd_describe(plan).split()[0] in ("igemm", "patch")
         finally:
             capi.conv_fwd_destroy(plan)
 
@@ -133,7 +133,7 @@ def test_config_table():
 
 def test_forced_config_dtype_and_vector_rules():
     n = capi.conv_fwd_num_configs()
-    d_bf16 = desc_from_problem(sd.problem(1, 1, 16, 16, (1, 6, 6), (1, 3, 3)), "bf16")
+    d_bf16 = desc_from_problem(sd.problem(1, 1, 32, 16, (1, 6, 6), (1, 3, 3), pad=(0, 1, 1)), "bf16")
     d_odd = desc_from_problem(sd.problem(1, 1, 5, 16, (1, 6, 6), (1, 3, 3)), "bf16")
     for i in range(n):
         name = capi.conv_fwd_config_name(i)
@@ -145,7 +145,7 @@ def test_forced_config_dtype_and_vector_rules():
         plan = capi.conv_fwd_create_with_config(d_bf16, i)
         assert name in capi.conv_fwd_describe(plan)
         capi.conv_fwd_destroy(plan)
-        if not name.endswith("_v1"):   # 16-byte channel vectors need C % 8 == 0
+        if not name.endswith("_v1"):   # 16-byte channel vectors / slices need C % 8 (16, 32) == 0
             with pytest.raises(ConvError):
                 capi.conv_fwd_create_with_config(d_odd, i)
     with pytest.raises(ConvError):
@@ -209,7 +209,7 @@ def test_selector_coefficients_match_compiled_configs():
     names = {line.split('"')[1] for line in open(inc) if line.strip().startswith('{"')}
     compiled = {capi.conv_fwd_config_name(i) for i in range(capi.conv_fwd_num_configs())}
     assert names and names <= compiled, names - compiled
-    dma = {n for n in compiled if "_dma_" in n}
+    dma = {n for n in compiled if "_dma_" in n or "_patch_" in n}
     assert dma <= names, dma - names
 
 

@@ -129,8 +129,11 @@ CONFIGS = _configs()
 
 
 def _ragged_problem(name):
-    C = 5 if name.endswith("_v1") else 24
-    # 2-D, M = 2*13*11 = 286, K = 40, Kred = 9*C (216 or 45), G = 2
+    # 2-D, 13 x 11 outputs (ragged against every tile and box), K = 40, G = 2
+    if "_patch_" in name:
+        C = 32        # a multiple of every patch kernel's channel slice
+    else:
+        C = 5 if name.endswith("_v1") else 24
     return sd.problem(2, 2, C, 40, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1))
 
 
@@ -154,8 +157,13 @@ def test_every_config_ragged(dev, cfg, name):
 @pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
 def test_every_config_3d_strided_dilated(dev, cfg, name):
     dt = "bf16" if name.startswith("bf16") else "f32"
-    C = 3 if name.endswith("_v1") else 16
-    p = sd.problem(3, 3, C, 20, (5, 9, 8), (3, 2, 3), (2, 1, 2), (2, 1, 3), (2, 3, 1))
+    if "_patch_" in name:
+        # the patch kernels take any depth stride/dilation/padding; in H and W
+        # a 3x3 filter at unit stride fits every configuration's patch
+        p = sd.problem(2, 2, 32, 40, (5, 10, 37), (3, 3, 3), (2, 1, 1), (2, 1, 1), (2, 1, 1))
+    else:
+        C = 3 if name.endswith("_v1") else 16
+        p = sd.problem(3, 3, C, 20, (5, 9, 8), (3, 2, 3), (2, 1, 2), (2, 1, 3), (2, 3, 1))
     x, w, b = sd.random_inputs(p, dt, 33, False)
     y, _ = run(dev, p, dt, x, w, None, False, config=cfg)
     assert_close(host(y), p, dt, x, w, None, False)
