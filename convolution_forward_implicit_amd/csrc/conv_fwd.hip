@@ -76,7 +76,7 @@ void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream
 
 FastDiv make_fastdiv(int d);
 
-template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX>
+template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX, int PAD>
 void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
                   hipEvent_t e1)
 {
@@ -93,13 +93,13 @@ void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStre
     const dim3 g(grid), b(256);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
-        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, true, true>), g, b, 0, s, e0, e1, 0, pp);
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, true, true>), g, b, 0, s, e0, e1, 0, pp);
     else if (bias)
-        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, true, false>), g, b, 0, s, e0, e1, 0, pp);
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, true, false>), g, b, 0, s, e0, e1, 0, pp);
     else if (kp.gelu)
-        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, false, true>), g, b, 0, s, e0, e1, 0, pp);
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, false, true>), g, b, 0, s, e0, e1, 0, pp);
     else
-        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, false, false>), g, b, 0, s, e0, e1, 0, pp);
+        hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, false, false>), g, b, 0, s, e0, e1, 0, pp);
 }
 
 enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2 };
@@ -134,23 +134,27 @@ struct TileCfg {
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
 // filter taps per depth tap.
-#define PATCH(TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX)                                  \
+#define PATCH(TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD)                             \
     TileCfg{1, KIND_PATCH, TH * TW, BN, CC, 4, 1, 8, NS,                                  \
-            PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX>::LDS_BYTES,              \
-            &launch_patch<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX>,                     \
-            "bf16_patch_" #TH "x" #TW "x" #BN "_c" #CC "_s" #NS "_p" #PHMAX "x" #PWMAX,   \
+            PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD>::LDS_BYTES,         \
+            &launch_patch<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD>,                \
+            "bf16_patch_" #TH "x" #TW "x" #BN "_c" #CC "_s" #NS "_p" #PHMAX "x" #PWMAX "_d" #PAD, \
             TH, TW, CC, PHMAX, PWMAX, TAPMAX}
 
 // One candidate table, shared by the selector, forced-config creation and
 // the sweeps.  VEC = 16 bytes of channels per load; the VEC = 1 entries serve
 // channel counts that are not a multiple of the vector.
 const TileCfg kCfgs[] = {
-    PATCH(8, 32, 64, 16, 2, 10, 34, 9),
-    PATCH(4, 32, 64, 16, 2, 6, 34, 9),
-    PATCH(8, 32, 32, 16, 2, 12, 36, 9),
-    PATCH(4, 32, 32, 16, 2, 8, 36, 9),
-    PATCH(8, 32, 64, 32, 2, 10, 34, 9),
-    PATCH(8, 16, 64, 16, 2, 10, 18, 9),
+    PATCH(8, 32, 64, 16, 2, 10, 34, 9, 1),
+    PATCH(4, 32, 64, 16, 2, 6, 34, 9, 1),
+    PATCH(8, 32, 32, 16, 2, 12, 36, 9, 1),
+    PATCH(8, 16, 64, 16, 2, 10, 18, 9, 1),
+    PATCH(8, 32, 64, 16, 2, 10, 34, 9, 0),
+    PATCH(8, 32, 64, 16, 3, 10, 34, 9, 0),
+    PATCH(8, 32, 32, 16, 2, 12, 36, 9, 0),
+    PATCH(8, 32, 32, 16, 3, 12, 36, 9, 0),
+    PATCH(8, 32, 64, 32, 2, 10, 34, 9, 0),
+    PATCH(16, 16, 64, 16, 2, 18, 18, 9, 0),
     DMA(1, 128, 128, 2, 2, 2, 32, 1),
     DMA(1, 128, 128, 2, 2, 2, 32, 2),
     DMA(1, 256, 64, 4, 1, 2, 32, 1),

@@ -16,11 +16,13 @@
 // tap is the patch read at a per-lane pixel offset plus a tap offset that is
 // the same for every lane.
 //
-// LDS rows (one patch pixel, or one weight (n, tap)) are CC channels plus one
-// 16-byte pad chunk, so the 8 lanes that read one 16-byte column of 8
-// neighbouring pixels hit different bank groups; the pad chunk is written by
-// an out-of-range (zero) load, which keeps each wave's 1 KB of LDS writes
-// contiguous.
+// LDS rows (one patch pixel, or one weight (n, tap)) are CC channels, plus
+// one 16-byte pad chunk when PAD = 1, so that the 8 lanes reading one
+// 16-byte column of 8 neighbouring rows hit different bank groups for any
+// stride; the pad chunk is written by an out-of-range (zero) load, which
+// keeps each wave's 1 KB of LDS writes contiguous.  Unpadded (PAD = 0) rows
+// are already conflict-free for unit width stride and an odd number of taps
+// (32-byte pixels, 32*taps-byte weight rows), at two thirds of the LDS.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,14 +41,14 @@ struct PatchParams {
     FastDiv fd_pw, fd_taps;
 };
 
-template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX>
+template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX, int PAD>
 struct PatchShape {
     static constexpr int NW = 4;                  // waves, splitting the box's pixels
     static constexpr int NT = NW * 64;
     static constexpr int BM = TH * TW;
     static constexpr int TM = BM / NW;            // pixels per wave
     static constexpr int MI = TM / 32, NI = BN / 32;
-    static constexpr int CPX = CC / 8 + 1;        // 16-byte chunks per LDS row (incl. pad)
+    static constexpr int CPX = CC / 8 + PAD;      // 16-byte chunks per LDS row (incl. pad)
     static constexpr int PITCH = CPX * 16;        // bytes per LDS row
     static constexpr int PATCH_LOADS = (PHMAX * PWMAX * CPX + 64 * NW - 1) / (64 * NW);  // per wave
     static constexpr int W_LOADS = (BN * TAPMAX * CPX + 64 * NW - 1) / (64 * NW);       // per wave
@@ -64,11 +66,11 @@ struct PatchShape {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
 
-template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX, bool BIAS, bool GELU>
+template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX, int PAD, bool BIAS, bool GELU>
 __global__ void __launch_bounds__(256)
 patch_conv_kernel(PatchParams pp)
 {
-    using S = PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX>;
+    using S = PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD>;
     const KParams &p = pp.k;
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS_BYTES];
@@ -115,7 +117,7 @@ patch_conv_kernel(PatchParams pp)
             const int pix = ci / S::CPX, q = ci - pix * S::CPX;
             const int r = fdiv(pix, pp.fd_pw), cpos = pix - r * pp.pw;
             const int ih = ih0 + r, iw = iw0 + cpos;
-            const bool ok = plane_ok && ci < npatch && q < S::CPX - 1 && (unsigned)ih < (unsigned)p.Hi &&
+            const bool ok = plane_ok && ci < npatch && q < CC / 8 && (unsigned)ih < (unsigned)p.Hi &&
                             (unsigned)iw < (unsigned)p.Wi;
             const int off = ((((nimg * p.Di + id) * p.Hi + ih) * p.Wi + iw) * GC) + g * p.C + cc + q * 8;
             dv[t] = ok ? (uint32_t)(off * 2) : kOutOfRange;
@@ -126,7 +128,7 @@ patch_conv_kernel(PatchParams pp)
             const int ci = lane + 64 * (wave + S::NW * t);
             const int row = ci / S::CPX, q = ci - row * S::CPX;
             const int n = fdiv(row, pp.fd_taps), tap = row - n * taps;
-            const bool ok = ci < nw && q < S::CPX - 1 && n0 + n < p.K;
+            const bool ok = ci < nw && q < CC / 8 && n0 + n < p.K;
             const int off = (g * p.K + n0 + n) * p.Kred + (z * taps + tap) * p.C + cc + q * 8;
             dv[S::PATCH_LOADS + t] = ok ? (uint32_t)(off * 2) : kOutOfRange;
         }
@@ -159,37 +161,57 @@ patch_conv_kernel(PatchParams pp)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // one K-step: every tap from the same patch, CC/16 k sub-steps per tap;
-    // the next stage's loads are issued after the first tap's products, so
-    // the remaining taps' products cover their latency
+    // One K-step: every tap from the same patch, CC/16 k sub-steps per tap,
+    // walked as one sequence of (tap, sub-step) pairs.  Fragments are read
+    // one pair ahead (two register sets), so each pair's LDS reads are in
+    // flight while the previous pair's products run.  The next stage's loads
+    // are issued after the first pair's products; the remaining pairs cover
+    // their latency.
+    constexpr int HS = CC / 16;
+    auto load_frags = [&](const unsigned char *P, const unsigned char *Wt, int pr, bf16x8_t (&a)[S::MI],
+                          bf16x8_t (&b)[S::NI]) {
+        const int tap = pr / HS, h = pr - tap * HS;
+        const int y = tap / p.X, x = tap - y * p.X;
+        const int toff = ((y * p.dh) * pp.pw + x * p.dw) * S::PITCH;
+        const int co = (2 * h + half) * 16;
+#pragma unroll
+        for (int i = 0; i < S::MI; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t *>(P + abase[i] + toff + co);
+#pragma unroll
+        for (int j = 0; j < S::NI; ++j)
+            b[j] = *reinterpret_cast<const bf16x8_t *>(Wt + (j * 32 + frow) * wrow + tap * S::PITCH + co);
+    };
+    auto mma = [&](const bf16x8_t (&a)[S::MI], const bf16x8_t (&b)[S::NI]) {
+#pragma unroll
+        for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < S::NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
     auto compute = [&](int stage, int dst) {
         const unsigned char *P = smem + stage * S::STAGE;
         const unsigned char *Wt = P + S::PATCH_BYTES;
-        for (int y = 0; y < p.Y; ++y)
-            for (int x = 0; x < p.X; ++x) {
-                const int toff = ((y * p.dh) * pp.pw + x * p.dw) * S::PITCH;
-                const int tap = y * p.X + x;
+        const int npairs = taps * HS;
+        bf16x8_t a0[S::MI], b0[S::NI], a1[S::MI], b1[S::NI];
+        load_frags(P, Wt, 0, a0, b0);
+        int pr = 0;
+        for (; pr + 1 < npairs; pr += 2) {
+            load_frags(P, Wt, pr + 1, a1, b1);
+            mma(a0, b0);
+            if (pr == 0 && dst >= 0) {
 #pragma unroll
-                for (int h = 0; h < CC / 16; ++h) {
-                    const int co = (2 * h + half) * 16;
-                    bf16x8_t a[S::MI], b[S::NI];
-#pragma unroll
-                    for (int i = 0; i < S::MI; ++i)
-                        a[i] = *reinterpret_cast<const bf16x8_t *>(P + abase[i] + toff + co);
-#pragma unroll
-                    for (int j = 0; j < S::NI; ++j)
-                        b[j] = *reinterpret_cast<const bf16x8_t *>(Wt + (j * 32 + frow) * wrow + tap * S::PITCH + co);
-#pragma unroll
-                    for (int i = 0; i < S::MI; ++i)
-#pragma unroll
-                        for (int j = 0; j < S::NI; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-                }
-                if (tap == 0 && dst >= 0) {
-#pragma unroll
-                    for (int t = 0; t < S::L; ++t) fire(dst, t);
-                }
+                for (int t = 0; t < S::L; ++t) fire(dst, t);
             }
+            if (pr + 2 < npairs) load_frags(P, Wt, pr + 2, a0, b0);
+            mma(a1, b1);
+        }
+        if (pr < npairs) {          // odd number of pairs: the last one is in a0/b0
+            mma(a0, b0);
+            if (pr == 0 && dst >= 0) {
+#pragma unroll
+                for (int t = 0; t < S::L; ++t) fire(dst, t);
+            }
+        }
     };
 
     // ---- pipeline ----------------------------------------------------------
