@@ -169,6 +169,28 @@ def test_every_config_3d_strided_dilated(dev, cfg, name):
     assert_close(host(y), p, dt, x, w, None, False)
 
 
+@pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
+def test_every_config_gelu_range(dev, cfg, name):
+    """The GELU epilogue over [-30, 30] (dense near 0 and in the negative
+    tail, where Phi is tiny): a centre-tap delta filter copies input channel
+    k mod C to output channel k, so each output is GELU of one input value."""
+    dt = "bf16" if name.startswith("bf16") else "f32"
+    p = _ragged_problem(name)
+    xs, ws, _, _ = ref.shapes(p)
+    n = int(np.prod(xs))
+    vals = np.concatenate([np.linspace(-30.0, 30.0, n // 4), np.linspace(-12.0, -3.0, n // 4),
+                           np.linspace(-1e-2, 1e-2, n // 4)])
+    vals = np.concatenate([vals, np.random.Generator(np.random.PCG64(61)).uniform(-6, 6, n - vals.size)])
+    x = np.random.Generator(np.random.PCG64(62)).permutation(vals).astype(np.float32).reshape(xs)
+    if dt == "bf16":
+        x = sd.round_bf16(x)
+    w = np.zeros(ws, dtype=np.float32)
+    for k in range(p["K"]):
+        w[:, k, 0, 1, 1, k % p["C"]] = 1.0
+    y, _ = run(dev, p, dt, x, w, None, True, config=cfg)
+    assert_close(host(y), p, dt, x, w, None, True)
+
+
 # --------------------------------------------------------------------------
 # Edge cases (selector's choice)
 EDGE = [
