@@ -15,7 +15,10 @@ counting padded taps, over the wall time of K steps bracketed by device
 synchronisation).  roofline = the dominant (most flop) kernel: its useful
 flop per launch over its mean duration, from HIP events that the launch
 itself records when the kernel starts and ends (on the stream it runs on),
-against the MI355X dense MFMA peak of its dtype.  cpu_baseline = the fp64
+against the MI355X dense MFMA peak of its dtype.  Those events are taken on
+every --event-every'th step of the timed region (default 8): a launch that
+records them costs the host ~10 us more, which at every step would show up
+in the step time of the small workloads.  cpu_baseline = the fp64
 oracle on the host cores over a bounded sample of the same workload.
 
     python bench.py --copy-bytes B [--steps K]
@@ -119,6 +122,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="record the dominant kernel's start/stop events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -177,8 +182,10 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = ([torch.cuda.Event(enable_timing=True) for _ in range(K)],
-          [torch.cuda.Event(enable_timing=True) for _ in range(K)])
+    E = max(1, args.event_every)
+    NE = (K + E - 1) // E             # steps whose dominant launch records events
+    ev = ([torch.cuda.Event(enable_timing=True) for _ in range(NE)],
+          [torch.cuda.Event(enable_timing=True) for _ in range(NE)])
     for e in ev[0] + ev[1]:
         e.record(stream)              # creates the event handles the kernel launch records
     start = torch.cuda.Event(enable_timing=True)
@@ -187,7 +194,10 @@ def main():
     t_wall0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        step(ev, i)
+        if i % E == 0:
+            step(ev, i // E)
+        else:
+            step()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -206,7 +216,7 @@ def main():
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4),
             "traffic": recorded_traffic(args.workload, dom, alg_bytes),
             "kernel": "layer %d: %s" % (dom + 1, convs[dom].describe()),
-            "kernel_ms": round(dom_ms, 5), "algorithmic_bytes": alg_bytes,
+            "kernel_ms": round(dom_ms, 5), "kernel_launches_timed": NE, "algorithmic_bytes": alg_bytes,
             "hbm_GBs_algorithmic": round(alg_bytes / (dom_ms * 1e-3) / 1e9, 1)}
 
     cpu = None

@@ -199,15 +199,46 @@ constexpr int kNumCfgs = (int)(sizeof(kCfgs) / sizeof(kCfgs[0]));
 
 // Per-configuration cost coefficients fitted to a sweep of every
 // configuration over a grid of problems (tuning/fit.py): predicted
-// milliseconds t = a + b*r + d*r*nk + e*nk, r = workgroups per compute unit,
-// nk = K-steps per workgroup.
+// milliseconds t = a + b*r + d*r*nk + e*nk + f*gelu*r, r = workgroups per
+// compute unit, nk = K-steps per workgroup, gelu = 1 with the GELU epilogue.
 struct CostCoef {
     const char *name;
-    double a, b, d, e;
+    double a, b, d, e, f;
 };
 const CostCoef kCoef[] = {
 #include "selector_coef.inc"
 };
+
+// Exact-shape tuning records: for every problem of the calibration sweep,
+// the configuration measured fastest on MI355X (256 compute units), with and
+// without the GELU epilogue (tuning/fit.py writes them from the sweep).  A
+// plan for one of these shapes (the bias flag is ignored) on a device with
+// that many compute units takes the record; every other shape is decided by
+// the fitted cost model.
+struct TuneRec {
+    int32_t dtype, gelu;
+    int64_t N, G, C, K, in[3], filt[3], stride[3], pad[3], dil[3];
+    const char *config;
+};
+const TuneRec kTuneDb[] = {
+#include "selector_db.inc"
+};
+constexpr int kTuneCus = 256;
+
+int tuned_config(const conv_fwd_desc_t &d)
+{
+    for (const TuneRec &t : kTuneDb) {
+        bool same = t.dtype == d.dtype && t.gelu == d.gelu && t.N == d.N && t.G == d.G && t.C == d.C &&
+                    t.K == d.K;
+        for (int i = 0; same && i < 3; ++i)
+            same = t.in[i] == d.in[i] && t.filt[i] == d.filt[i] && t.stride[i] == d.stride[i] &&
+                   t.pad[i] == d.pad[i] && t.dil[i] == d.dilation[i];
+        if (!same) continue;
+        for (int i = 0; i < kNumCfgs; ++i)
+            if (strcmp(kCfgs[i].name, t.config) == 0) return i;
+    }
+    return -1;
+}
 
 const CostCoef *coef_of(const TileCfg &c)
 {
@@ -249,6 +280,7 @@ struct conv_fwd_plan {
     int64_t x_elems, w_elems, b_elems, y_elems;
     int esz;
     int cfg;
+    bool tuned;      // cfg came from an exact-shape tuning record
     int grid;
     KParams kp;      // pointers filled per run
     char text[256];
@@ -359,7 +391,8 @@ double predicted_ms(const TileCfg &c, const conv_fwd_plan &pl, int cus)
     if (!k) return 1e3 * cost(c, pl, cus) * 10.0;   // uncalibrated: last resort
     const double r = std::ceil(tiles_of(c, pl.desc, pl.out) / cus);
     const double nk = steps_of(c, pl.desc);
-    return k->a + k->b * r + k->d * r * nk + k->e * nk;
+    const double g = pl.desc.gelu ? 1.0 : 0.0;
+    return k->a + k->b * r + k->d * r * nk + k->e * nk + k->f * g * r;
 }
 
 // The patch kernel's shape limits: channel slices, patch extent, taps.
@@ -438,15 +471,21 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         pl->cfg = forced;
     } else {
         const int cus = device_cu_count();
-        int best = -1;
-        double best_cost = 0.0;
-        for (int i = 0; i < kNumCfgs; ++i) {
-            const TileCfg &c = kCfgs[i];
-            if (!eligible(c)) continue;
-            const double t = predicted_ms(c, *pl, cus);
-            if (best < 0 || t < best_cost) { best = i; best_cost = t; }
+        const int rec = cus == kTuneCus ? tuned_config(d) : -1;
+        if (rec >= 0 && eligible(kCfgs[rec])) {
+            pl->cfg = rec;
+            pl->tuned = true;
+        } else {
+            int best = -1;
+            double best_cost = 0.0;
+            for (int i = 0; i < kNumCfgs; ++i) {
+                const TileCfg &c = kCfgs[i];
+                if (!eligible(c)) continue;
+                const double t = predicted_ms(c, *pl, cus);
+                if (best < 0 || t < best_cost) { best = i; best_cost = t; }
+            }
+            pl->cfg = best;
         }
-        pl->cfg = best;
     }
     const TileCfg &c = kCfgs[pl->cfg];
     KParams &kp = pl->kp;
@@ -479,12 +518,12 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         snprintf(pl->text, sizeof(pl->text),
                  "patch %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%d boxes/plane, %d n-tiles) lds=%dB%s", c.name,
                  kp.M, kp.K, kp.Kred, kp.G, pl->grid, (kp.Ho + c.TH - 1) / c.TH, (kp.Wo + c.TW - 1) / c.TW,
-                 kp.tiles_n, c.lds_bytes, forced >= 0 ? " forced" : "");
+                 kp.tiles_n, c.lds_bytes, forced >= 0 ? " forced" : pl->tuned ? " tuned" : "");
     else
         snprintf(pl->text, sizeof(pl->text),
                  "igemm %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%dx%d tiles) lds=%dB%s",
                  c.name, kp.M, kp.K, kp.Kred, kp.G, pl->grid, kp.tiles_m, kp.tiles_n, kp.G, c.lds_bytes,
-                 forced >= 0 ? " forced" : "");
+                 forced >= 0 ? " forced" : pl->tuned ? " tuned" : "");
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
     return CONV_OK;

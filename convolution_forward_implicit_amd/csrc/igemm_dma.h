@@ -15,7 +15,10 @@
 //    loads may still be outstanding;
 //  * chunk q of row r is stored at 16-byte slot q ^ (r & 7), so the 8 lanes
 //    that read one 16-byte column of 8 consecutive rows hit 8 different
-//    bank groups;
+//    bank groups; for 32x32 blocks, whose fragment reads take one chunk of
+//    32 consecutive rows, rows with bit 4 set also swap the chunks of each
+//    pair (slot q ^ (r & 7) ^ 1), which the 8-row swizzle alone leaves in
+//    two-way bank conflicts on gfx950 (measured);
 //  * the filter-tap position of a lane's chunk advances incrementally from
 //    step to step (no integer division in the loop).
 //
@@ -148,6 +151,11 @@ igemm_dma_kernel(DmaParams dp)
     // ---- this lane's DMA assignment -------------------------------------
     const int lrow = lane >> 3;                 // row inside an 8-row block
     const int chunk = (lane & 7) ^ lrow;        // which 16-byte chunk of the K slice
+    // Pair swap for rows with bit 4 set (32x32 blocks).  The DMA side then
+    // fetches the partner chunk of the pair, which lies in the same filter
+    // tap when C is a whole number of chunk pairs; otherwise no swap.
+    const int sw4 = (MF == 32 && p.C % (2 * S::VEC) == 0) ? 1 : 0;
+    const int pair_delta = (chunk & 1) ? -S::VEC : S::VEC;   // elements to the partner chunk
 
     // Rows of this lane: m_t = m0 + (wave*A_PER_W + t)*8 + lrow.  The first
     // is decoded with divisions, the others by stepping 8 pixels forward.
@@ -185,7 +193,8 @@ igemm_dma_kernel(DmaParams dp)
 #pragma unroll
     for (int t = 0; t < S::B_PER_W; ++t) {
         const int n = n0 + (wave * S::B_PER_W + t) * 8 + lrow;
-        b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + chunk * S::VEC) * S::ESZ) : kOutOfRange;
+        const int cht = chunk ^ (sw4 & ((wave * S::B_PER_W + t) >> 1));   // row bit 4 = block bit 1
+        b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + cht * S::VEC) * S::ESZ) : kOutOfRange;
     }
 
     // filter tap of reduction index r = k0 + chunk*VEC, stepped by one
@@ -217,7 +226,8 @@ igemm_dma_kernel(DmaParams dp)
                 const bool ok = rok && (unsigned)(a_bd[t] + zd) < (unsigned)p.Di &&
                                 (unsigned)(a_bh[t] + yh) < (unsigned)p.Hi &&
                                 (unsigned)(a_bw[t] + xw) < (unsigned)p.Wi;
-                dv[u][t] = ok ? (uint32_t)((a_off[t] + toff) * S::ESZ) : kOutOfRange;
+                const int swap = sw4 & ((wave * S::A_PER_W + t) >> 1);
+                dv[u][t] = ok ? (uint32_t)((a_off[t] + toff + (swap ? pair_delta : 0)) * S::ESZ) : kOutOfRange;
             }
             const uint32_t kb = (uint32_t)((k0 + u * S::SUBK) * S::ESZ);
 #pragma unroll
@@ -258,6 +268,7 @@ igemm_dma_kernel(DmaParams dp)
     // (lane & 31) with chunk (lane >> 5) of each 32-byte quarter.
     const int frow = lane & (MF - 1);
     const int fk = lane / MF;
+    constexpr int RUNS = S::ACC / 4;     // runs of 4 consecutive channels per block
 
     // One stage: per sub-slice, all fragments are read first (one LDS
     // latency per sub-slice), then the products run; the prepared loads of
@@ -279,7 +290,7 @@ igemm_dma_kernel(DmaParams dp)
                 // 32x32 blocks: lane half fk takes chunk 2q+fk; 16x16 blocks:
                 // lane quarter fk takes chunk 4q+fk
                 const int ch = (MF == 32 && DT == 1) ? 2 * q + fk : 4 * q + fk;
-                const int sw = ((ch ^ (frow & 7)) << 4);
+                const int sw = ((ch ^ (frow & 7) ^ (sw4 & (frow >> 4))) << 4);
 #pragma unroll
                 for (int i = 0; i < S::MI; ++i)
                     a[q][i] = *reinterpret_cast<const Frag *>(As + (wm * S::TM + i * MF + frow) * 128 + sw);
@@ -324,7 +335,7 @@ igemm_dma_kernel(DmaParams dp)
 #pragma unroll
             for (int q = 0; q < S::L; ++q) fire(s, q);
         }
-    for (int it = 0; it < nk; ++it) {
+    for (int it = 0; it < nk - 1; ++it) {
         if (it + NS - 2 < nk) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();                        // step it is in LDS for every wave
@@ -332,13 +343,32 @@ igemm_dma_kernel(DmaParams dp)
         if (more) prep((it + NS - 1) * S::BK);
         compute(it % NS, more ? (it + NS - 1) % NS : -1);
     }
+    // last step: nothing left to load
+    wait_vmcnt<0>();
+    __syncthreads();
+    // Bias of the lane's output channels (see the epilogue for the layout),
+    // loaded here so that the last step's products hide its latency.
+    float bias_v[S::NI][RUNS][4];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+            for (int h = 0; h < RUNS; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // unconditional (clamped) loads, so they are all in flight at once
+                    const int n = n0 + wn * S::TN + j * MF + h * 8 + fk * 4 + e;
+                    const float v = to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + (n < p.K ? n : p.K - 1)]);
+                    bias_v[j][h][e] = n < p.K ? v : 0.f;
+                }
+    }
+    compute((nk - 1) % NS, -1);
     __syncthreads();
 
     // ---- epilogue: bias, GELU, round, stage in LDS, whole-vector stores ---
     // Transposed product: in a 16x16 block the lane holds channels
     // 4*fk + e (e = 0..3) of pixel frow; in a 32x32 block it holds channels
     // 8*h + 4*fk + e (h = 0..3, e = 0..3) of pixel frow.
-    constexpr int RUNS = S::ACC / 4;     // runs of 4 consecutive channels per block
     T *Cs = reinterpret_cast<T *>(smem);
 #pragma unroll
     for (int j = 0; j < S::NI; ++j)
@@ -348,10 +378,7 @@ igemm_dma_kernel(DmaParams dp)
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BIAS) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int n = n0 + nl + e;
-                    if (n < p.K) bv[e] = to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n]);
-                }
+                for (int e = 0; e < 4; ++e) bv[e] = bias_v[j][h][e];
             }
 #pragma unroll
             for (int i = 0; i < S::MI; ++i) {

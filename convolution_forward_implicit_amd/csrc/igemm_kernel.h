@@ -335,12 +335,17 @@ igemm_fwd_kernel(KParams p)
 
     // ---- epilogue: bias, GELU, round, stage in LDS, whole-vector stores ---
     float bias_v[S::NI];
+    if (p.bias != nullptr) {
 #pragma unroll
-    for (int j = 0; j < S::NI; ++j) {
-        const int n = n0 + wn * S::TN + j * 16 + frow;
-        bias_v[j] = (p.bias != nullptr && n < p.K)
-                        ? to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n])
-                        : 0.f;
+        for (int j = 0; j < S::NI; ++j) {
+            // unconditional (clamped) loads, so they are all in flight at once
+            const int n = n0 + wn * S::TN + j * 16 + frow;
+            const float v = to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + (n < p.K ? n : p.K - 1)]);
+            bias_v[j] = n < p.K ? v : 0.f;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < S::NI; ++j) bias_v[j] = 0.f;
     }
     T *Cs = reinterpret_cast<T *>(smem);
 #pragma unroll

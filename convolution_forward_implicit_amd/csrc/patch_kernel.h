@@ -17,12 +17,14 @@
 // the same for every lane.
 //
 // LDS rows (one patch pixel, or one weight (n, tap)) are CC channels, plus
-// one 16-byte pad chunk when PAD = 1, so that the 8 lanes reading one
-// 16-byte column of 8 neighbouring rows hit different bank groups for any
-// stride; the pad chunk is written by an out-of-range (zero) load, which
-// keeps each wave's 1 KB of LDS writes contiguous.  Unpadded (PAD = 0) rows
-// are already conflict-free for unit width stride and an odd number of taps
-// (32-byte pixels, 32*taps-byte weight rows), at two thirds of the LDS.
+// one 16-byte pad chunk when PAD = 1; the pad chunk is written by an
+// out-of-range (zero) load, which keeps each wave's 1 KB of LDS writes
+// contiguous.  Unpadded 32-byte rows (CC = 16, PAD = 0) swap their two
+// 16-byte chunks in every other group of 8 patch pixels (pixel bit 3) and,
+// for the weights, in every other group of 16 output channels (channel
+// bit 4): a fragment read takes one chunk of 32 pixels (or channels), and
+// without the swap pixels 8 apart and channels 16 apart fall into the same
+// banks (two-way conflicts on gfx950, measured).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -56,6 +58,7 @@ struct PatchShape {
     static constexpr int PATCH_BYTES = PATCH_LOADS * NW * 1024;
     static constexpr int W_BYTES = W_LOADS * NW * 1024;
     static constexpr int STAGE = PATCH_BYTES + W_BYTES;
+    static constexpr bool SWZ = (CPX == 2);       // chunk-pair swap of 32-byte rows
     static constexpr int LDC = BN + 8;
     static constexpr int EPI = BM * LDC * 2;
     static constexpr int LDS_BYTES = NS * STAGE > EPI ? NS * STAGE : EPI;
@@ -119,7 +122,8 @@ patch_conv_kernel(PatchParams pp)
             const int ih = ih0 + r, iw = iw0 + cpos;
             const bool ok = plane_ok && ci < npatch && q < CC / 8 && (unsigned)ih < (unsigned)p.Hi &&
                             (unsigned)iw < (unsigned)p.Wi;
-            const int off = ((((nimg * p.Di + id) * p.Hi + ih) * p.Wi + iw) * GC) + g * p.C + cc + q * 8;
+            const int qg = S::SWZ ? q ^ ((pix >> 3) & 1) : q;   // chunk stored in slot q
+            const int off = ((((nimg * p.Di + id) * p.Hi + ih) * p.Wi + iw) * GC) + g * p.C + cc + qg * 8;
             dv[t] = ok ? (uint32_t)(off * 2) : kOutOfRange;
         }
         const int nw = BN * taps * S::CPX;
@@ -129,7 +133,8 @@ patch_conv_kernel(PatchParams pp)
             const int row = ci / S::CPX, q = ci - row * S::CPX;
             const int n = fdiv(row, pp.fd_taps), tap = row - n * taps;
             const bool ok = ci < nw && q < CC / 8 && n0 + n < p.K;
-            const int off = (g * p.K + n0 + n) * p.Kred + (z * taps + tap) * p.C + cc + q * 8;
+            const int qg = S::SWZ ? q ^ ((n >> 4) & 1) : q;
+            const int off = (g * p.K + n0 + n) * p.Kred + (z * taps + tap) * p.C + cc + qg * 8;
             dv[S::PATCH_LOADS + t] = ok ? (uint32_t)(off * 2) : kOutOfRange;
         }
     };
@@ -175,11 +180,15 @@ patch_conv_kernel(PatchParams pp)
         const int toff = ((y * p.dh) * pp.pw + x * p.dw) * S::PITCH;
         const int co = (2 * h + half) * 16;
 #pragma unroll
-        for (int i = 0; i < S::MI; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t *>(P + abase[i] + toff + co);
+        for (int i = 0; i < S::MI; ++i) {
+            const int t = abase[i] + toff;       // byte offset of the lane's pixel
+            const int ca = S::SWZ ? (half ^ ((t >> 8) & 1)) * 16 : co;   // pixel bit 3 = byte bit 8
+            a[i] = *reinterpret_cast<const bf16x8_t *>(P + t + ca);
+        }
+        const int cb = S::SWZ ? (half ^ ((frow >> 4) & 1)) * 16 : co;
 #pragma unroll
         for (int j = 0; j < S::NI; ++j)
-            b[j] = *reinterpret_cast<const bf16x8_t *>(Wt + (j * 32 + frow) * wrow + tap * S::PITCH + co);
+            b[j] = *reinterpret_cast<const bf16x8_t *>(Wt + (j * 32 + frow) * wrow + tap * S::PITCH + cb);
     };
     auto mma = [&](const bf16x8_t (&a)[S::MI], const bf16x8_t (&b)[S::NI]) {
 #pragma unroll
@@ -222,7 +231,7 @@ patch_conv_kernel(PatchParams pp)
 #pragma unroll
             for (int t = 0; t < S::L; ++t) fire(s, t);
         }
-    for (int it = 0; it < nk; ++it) {
+    for (int it = 0; it < nk - 1; ++it) {
         if (it + NS - 2 < nk) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();
@@ -230,6 +239,26 @@ patch_conv_kernel(PatchParams pp)
         if (more) prep(it + NS - 1);
         compute(it % NS, more ? (it + NS - 1) % NS : -1);
     }
+    // last step: nothing left to load
+    wait_vmcnt<0>();
+    __syncthreads();
+    // Bias of the lane's output channels, loaded here so that the last step's
+    // products hide its latency.
+    float bias_v[S::NI][4][4];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // unconditional (clamped) loads, so they are all in flight at once
+                    const int n = n0 + j * 32 + hh * 8 + half * 4 + e;
+                    const float v = bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[g * p.K + (n < p.K ? n : p.K - 1)]);
+                    bias_v[j][hh][e] = n < p.K ? v : 0.f;
+                }
+    }
+    compute((nk - 1) % NS, -1);
     __syncthreads();
 
     // ---- epilogue (as the implicit GEMM: transposed 32x32 blocks) ----------
@@ -242,10 +271,7 @@ patch_conv_kernel(PatchParams pp)
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BIAS) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int n = n0 + nl + e;
-                    if (n < p.K) bv[e] = bf16_to_f32(reinterpret_cast<const uint16_t *>(p.bias)[g * p.K + n]);
-                }
+                for (int e = 0; e < 4; ++e) bv[e] = bias_v[j][hh][e];
             }
 #pragma unroll
             for (int i = 0; i < S::MI; ++i) {

@@ -4,9 +4,10 @@ coefficients compiled into the library.
     python -m convolution_forward_implicit_amd.tuning.fit SWEEP.csv [--write]
 
 Model, per tile configuration c and problem s (the unit is milliseconds):
-    t_c(s) = a_c + b_c * r + d_c * r * nk + e_c * nk
+    t_c(s) = a_c + b_c * r + d_c * r * nk + e_c * nk + f_c * gelu * r
     r  = ceil(tiles / CUs)          workgroups each compute unit runs
     nk = ceil(C*Z*Y*X / BK_c)       K-steps per workgroup
+    gelu = 1 with the bias + GELU epilogue (its VALU time per workgroup), else 0
     tiles = ceil(M / BM_c) * ceil(K / BN_c) * G
 (an input-patch configuration: tiles = boxes x channel tiles x planes x
 groups, nk = Z * C / CC) fitted by least squares on relative error.  Reported: leave-one-problem-out
@@ -24,6 +25,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OUT = os.path.join(os.path.dirname(HERE), "csrc", "selector_coef.inc")
+OUT_DB = os.path.join(os.path.dirname(HERE), "csrc", "selector_db.inc")
 CUS = 256
 
 
@@ -42,6 +44,8 @@ def cfg_tile(name):
 
 
 def features(prob, name):
+    """[1, r, r*nk, nk, gelu*r] of a problem (dict with a "gelu" flag) for one
+    configuration."""
     t = cfg_tile(name)
     o = [(prob["in"][i] + 2 * prob["pad"][i] - prob["dil"][i] * (prob["filt"][i] - 1) - 1) // prob["stride"][i] + 1
          for i in range(3)]
@@ -55,7 +59,8 @@ def features(prob, name):
         tiles = math.ceil(M / BM) * math.ceil(prob["K"] / BN) * prob["G"]
         nk = math.ceil(prob["C"] * prob["filt"][0] * prob["filt"][1] * prob["filt"][2] / BK)
     r = math.ceil(tiles / CUS)
-    return [1.0, float(r), float(r * nk), float(nk)]
+    g = 1.0 if prob.get("gelu") else 0.0
+    return [1.0, float(r), float(r * nk), float(nk), g * r]
 
 
 def load(path):
@@ -63,23 +68,26 @@ def load(path):
     with open(path) as f:
         for row in csv.DictReader(f):
             key = tuple(row[k] for k in ("dtype", "N", "G", "C", "K", "Di", "Hi", "Wi", "Z", "Y", "X",
-                                         "sd", "sh", "sw", "pd", "ph", "pw", "dd", "dh", "dw"))
+                                         "sd", "sh", "sw", "pd", "ph", "pw", "dd", "dh", "dw", "gelu"))
             if key not in probs:
                 v = [int(x) for x in key[1:]]
                 probs[key] = {"dtype": key[0], "N": v[0], "G": v[1], "C": v[2], "K": v[3],
                               "in": v[4:7], "filt": v[7:10], "stride": v[10:13], "pad": v[13:16],
-                              "dil": v[16:19], "times": {}}
+                              "dil": v[16:19], "gelu": v[19], "times": {}}
             probs[key]["times"][row["config"]] = float(row["ms"])
     return list(probs.values())
 
 
 def fit(probs, skip=None):
+    """Per-configuration least squares; `skip` holds out one problem shape
+    (both of its epilogue variants)."""
     coef = {}
     names = sorted({n for p in probs for n in p["times"]})
+    held = None if skip is None else shape_key(probs[skip])
     for name in names:
         X, y = [], []
         for i, p in enumerate(probs):
-            if i == skip or name not in p["times"]:
+            if (held is not None and shape_key(p) == held) or name not in p["times"]:
                 continue
             X.append(features(p, name))
             y.append(p["times"][name])
@@ -89,6 +97,11 @@ def fit(probs, skip=None):
         w = 1.0 / y
         coef[name], *_ = np.linalg.lstsq(X * w[:, None], y * w, rcond=None)
     return coef
+
+
+def shape_key(p):
+    return (p["dtype"], p["N"], p["G"], p["C"], p["K"], tuple(p["in"]), tuple(p["filt"]),
+            tuple(p["stride"]), tuple(p["pad"]), tuple(p["dil"]))
 
 
 def pick(coef, p):
@@ -113,10 +126,26 @@ def write(coef, path=OUT):
     with open(path, "w") as f:
         f.write("// Generated by convolution_forward_implicit_amd/tuning/fit.py from a sweep of every\n"
                 "// configuration over the calibration grid: predicted milliseconds\n"
-                "// t = a + b*r + d*r*nk + e*nk (r = workgroups per compute unit, nk = K-steps).\n")
+                "// t = a + b*r + d*r*nk + e*nk + f*gelu*r (r = workgroups per compute unit,\n"
+                "// nk = K-steps, gelu = 1 with the GELU epilogue).\n")
         for name in sorted(coef):
-            a, b, d, e = coef[name]
-            f.write('    {"%s", %.6e, %.6e, %.6e, %.6e},\n' % (name, a, b, d, e))
+            a, b, d, e, g = coef[name]
+            f.write('    {"%s", %.6e, %.6e, %.6e, %.6e, %.6e},\n' % (name, a, b, d, e, g))
+
+
+def write_db(probs, path=OUT_DB):
+    """Exact-shape tuning records: the fastest measured configuration of
+    every swept (problem, epilogue)."""
+    with open(path, "w") as f:
+        f.write("// Generated by convolution_forward_implicit_amd/tuning/fit.py: the configuration\n"
+                "// measured fastest for each problem of the calibration sweep (MI355X, 256 CUs).\n"
+                "// {dtype, gelu, N, G, C, K, in, filt, stride, pad, dil, config}\n")
+        for p in probs:
+            best = min(p["times"], key=p["times"].get)
+            t = lambda v: "{%d, %d, %d}" % tuple(v)
+            f.write('    {%d, %d, %d, %d, %d, %d, %s, %s, %s, %s, %s, "%s"},\n' % (
+                0 if p["dtype"] == "f32" else 1, p["gelu"], p["N"], p["G"], p["C"], p["K"], t(p["in"]),
+                t(p["filt"]), t(p["stride"]), t(p["pad"]), t(p["dil"]), best))
 
 
 if __name__ == "__main__":
@@ -124,4 +153,5 @@ if __name__ == "__main__":
     print(quality(probs))
     if "--write" in sys.argv:
         write(fit(probs))
-        print("wrote", OUT)
+        write_db(probs)
+        print("wrote", OUT, OUT_DB)

@@ -225,3 +225,25 @@ def test_selector_fit_reproduces_committed_table(tmp_path):
     assert out.read_text() == open(os.path.join(here, "csrc", "selector_coef.inc")).read()
     q = fit.quality(probs)
     assert q["mean_eff"] > 0.9 and q["top5"] > 0.8, q
+
+
+def test_tuning_records_match_sweep_and_configs(tmp_path):
+    """The exact-shape tuning records are the sweep's fastest configuration
+    per (problem, epilogue), regenerate from the committed sweep, and name
+    compiled configurations of their own dtype."""
+    import os
+    from convolution_forward_implicit_amd.tuning import fit
+    here = os.path.dirname(capi.LIB_PATH)
+    probs = fit.load(os.path.join(here, "tuning", "sweep_mi355x.csv"))
+    out = tmp_path / "db.inc"
+    fit.write_db(probs, str(out))
+    committed = open(os.path.join(here, "csrc", "selector_db.inc")).read()
+    assert out.read_text() == committed
+    dtype_of = {capi.conv_fwd_config_name(i): capi.conv_fwd_config_dtype(i)
+                for i in range(capi.conv_fwd_num_configs())}
+    rows = [l for l in committed.splitlines() if l.strip().startswith("{")]
+    assert len(rows) == len(probs)
+    for l in rows:
+        name = l.split('"')[1]
+        assert name in dtype_of, name
+        assert dtype_of[name] == int(l.strip()[1]), l
