@@ -66,6 +66,40 @@ def check(got, ref, absdot, p, dtype, has_bias, gelu):
     }
 
 
+def check_chain(got, ref, absdot2, carry, p1, p2, gelu):
+    """Parity of a fused two-conv chain (bf16), whose intermediate h never
+    leaves the device, so the oracle rounds its own exact h to bf16.  The
+    device's h may then differ from the oracle's by the fp32 accumulation
+    error of conv1 plus one bf16 rounding step (2^-7 relative), and conv2
+    carries that into y:
+
+        |g - r| <= rtol |r| + L gamma_n2 absdot2
+                   + L (2^-7 (absdot2 - |b2|) + L gamma_n1 carry)
+
+    with absdot2 = |b2| + sum |w2 h| and carry = sum |w2| absdot1 (from
+    oracle.ref.conv_chain).  The |b2| part is left in the 2^-7 term (a
+    slightly looser bound)."""
+    got = np.asarray(got, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    absdot2 = np.asarray(absdot2, dtype=np.float64).ravel()
+    carry = np.asarray(carry, dtype=np.float64).ravel()
+    lip = 1.13 if gelu else 1.0
+    lim = (RTOL["bf16"] * np.abs(ref) + lip * gamma(reduction_length(p2, True)) * absdot2
+           + lip * (2.0 ** -7 * absdot2 + lip * gamma(reduction_length(p1, True)) * carry))
+    err = np.abs(got - ref)
+    finite = np.isfinite(got)
+    plain = bound(ref, absdot2, p2, "bf16", True, gelu)
+    return {
+        "ok": bool(finite.all() and (err <= lim).all()),
+        "n": int(got.size),
+        "n_fail": int((~(err <= lim)).sum() + (~finite).sum()),
+        "max_ratio": float((err / np.where(lim > 0, lim, 1.0)).max()) if got.size else 0.0,
+        "within_single_call_bound": float((err <= plain).mean()) if got.size else 1.0,
+        "max_abs_diff": float(err.max()) if got.size else 0.0,
+        "limit": lim,
+    }
+
+
 def round_to_bf16_bits(v):
     """IEEE round-to-nearest-even of float32-exact values to bfloat16, as
     uint16 bit patterns (NaN stays NaN).  Used to form the expected output of

@@ -17,7 +17,9 @@ shape and the page's dispatch shapes; an independent numpy brute force
 (explicit zero padding, zero-inserted dilated kernel); torch fp64 conv;
 conv1d == conv2d(H=1) == conv3d(D=H=1); grouped == G independent convs;
 delta kernel; all-ones border counts; 1x1 conv == matmul; single-channel
-conv == numpy.correlate; linearity; GELU closed forms.
+conv == numpy.correlate; linearity; GELU closed forms; bf16 rounding against
+IEEE bit patterns and hand-worked ties; the two-conv chain against delta
+filters (closed form) and against the composed 5-tap kernel (interior).
 """
 import ctypes
 import math
@@ -140,6 +142,87 @@ def conv_fwd_points(p, x, w, b, gelu, flat_idx):
     if rc != 0:
         raise ValueError("oracle_conv_fwd_points failed (%d)" % rc)
     return y, ad
+
+
+def round_bf16(v):
+    """Exact values -> the nearest bfloat16 (ties to even), as float64:
+    8 significant bits, float32's exponent range (normal from 2^-126,
+    subnormals in steps of 2^-133), overflow to infinity.  Rounds the exact
+    value once (no detour through float32)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    a = np.abs(v)
+    big = a >= 2.0 ** -126
+    m, e = np.frexp(v[big])                       # v = m * 2^e, 0.5 <= |m| < 1
+    out[big] = np.ldexp(np.rint(m * 256.0), e - 8)  # numpy rint: half to even
+    out[~big] = np.rint(v[~big] * 2.0 ** 133) * 2.0 ** -133
+    maxb = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    # beyond the largest finite bf16 (after rounding) the result is infinite
+    out[np.abs(out) > maxb] = np.copysign(np.inf, v[np.abs(out) > maxb])
+    return out
+
+
+def chain_problems(p1, p2):
+    """Check that p2 reads p1's output (same batch, p2.C == p1.K, p2's input
+    extent == p1's output extent, one group)."""
+    if p1["G"] != 1 or p2["G"] != 1 or p1["N"] != p2["N"] or p2["C"] != p1["K"]:
+        raise ValueError("second conv must read the first one's output")
+    if tuple(p2["in"]) != tuple(out_dims(p1)):
+        raise ValueError("second conv's input extent %r != first conv's output %r"
+                         % (tuple(p2["in"]), tuple(out_dims(p1))))
+
+
+def conv_chain(p1, p2, x, w1, b1, w2, b2, gelu):
+    """Two convolutions in a row, the way the conv frontend of the ExecuTorch
+    conv1d issue (table of the two-conv frontend) runs them: h = conv1(x)
+    (+ b1, GELU), rounded to bfloat16 (the intermediate has the call's
+    dtype), then y = conv2(h) (+ b2, GELU), unrounded.
+    Returns (y, absdot2, carry): absdot2 = |b2| + sum|w2 h| per output, and
+    carry = sum|w2| * absdot1 over the h values each output reads (absdot1 =
+    |b1| + sum|w1 x| of that h value), which bounds how the fp32
+    accumulation error of h propagates into y."""
+    chain_problems(p1, p2)
+    h, ad1 = conv_fwd(p1, x, w1, b1, gelu)
+    hr = round_bf16(h)
+    y, ad2 = conv_fwd(p2, hr, w2, b2, gelu)
+    carry = conv_fwd(p2, ad1, np.abs(np.asarray(w2, dtype=np.float64)), None, False, want_absdot=False)
+    return y, ad2, carry
+
+
+def conv_chain_points(p1, p2, x, w1, b1, w2, b2, gelu, flat_idx):
+    """conv_chain at flat output indices of y: only the h values those
+    outputs read are computed (the rest of h stays zero and is never read)."""
+    chain_problems(p1, p2)
+    idx = np.asarray(flat_idx, dtype=np.int64)
+    _, ws2, _, ys2 = shapes(p2)
+    _, _, _, hs = shapes(p1)
+    N, Do, Ho, Wo, _, K2 = ys2
+    Z, Y, X = p2["filt"]
+    sd, sh, sw = p2["stride"]
+    pd, ph, pw = p2["pad"]
+    dd, dh, dw = p2["dil"]
+    Dh, Hh, Wh = hs[1], hs[2], hs[3]
+    rest, ow = np.divmod(idx // K2, Wo)
+    rest, oh = np.divmod(rest, Ho)
+    nb, od = np.divmod(rest, Do)
+    pix = set()
+    for z in range(Z):
+        for yy in range(Y):
+            for xx in range(X):
+                di, hi, wi = od * sd - pd + z * dd, oh * sh - ph + yy * dh, ow * sw - pw + xx * dw
+                ok = (di >= 0) & (di < Dh) & (hi >= 0) & (hi < Hh) & (wi >= 0) & (wi < Wh)
+                pix.update(((nb[ok] * Dh + di[ok]) * Hh + hi[ok]) * Wh + wi[ok])
+    pix = np.array(sorted(pix), dtype=np.int64)
+    C2 = p2["C"]
+    hidx = (pix[:, None] * C2 + np.arange(C2)[None, :]).ravel()
+    hv, ad1 = conv_fwd_points(p1, x, w1, b1, gelu, hidx)
+    h = np.zeros(int(np.prod(hs)), dtype=np.float64)
+    a1 = np.zeros_like(h)
+    h[hidx] = round_bf16(hv)
+    a1[hidx] = ad1
+    y, ad2 = conv_fwd_points(p2, h, w2, b2, gelu, idx)
+    carry, _ = conv_fwd_points(p2, a1, np.abs(np.asarray(w2, dtype=np.float64)), None, False, idx)
+    return y, ad2, carry
 
 
 def max_threads():

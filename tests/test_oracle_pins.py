@@ -333,3 +333,134 @@ def test_workload_generation_is_seeded_and_bf16_exact():
     assert w3["x"].shape == (32, 1, 1, 3000, 1, 80)
     assert w3["w"][1].shape == (1, 384, 1, 1, 3, 384)
     assert abs(float(np.std(w3["w"][1])) - 1 / math.sqrt(1152)) < 2e-3
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding of exact values and the two-conv chain (fused frontend)
+def test_round_bf16_against_bit_patterns_and_hand_ties():
+    rng = np.random.Generator(np.random.PCG64(71))
+    v = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-30, 30, 5000),
+                        [0.0, -0.0, 1.0, -2.5, 2.0 ** -126, 2.0 ** -130, 65504.0]]).astype(np.float32)
+    got = ref.round_bf16(v.astype(np.float64))
+    want = check.bf16_bits_to_f64(check.round_to_bf16_bits(v.astype(np.float64)))
+    assert np.array_equal(got, want)
+    # ties (values between two bf16 neighbours, exactly half way) go to even
+    hand = {1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, -(1 + 2 ** -8): -1.0,
+            2 ** -134: 0.0, 3 * 2 ** -134: 2 ** -132, 1 + 2 ** -8 + 2 ** -40: 1 + 2 ** -7}
+    for a, b in hand.items():
+        assert ref.round_bf16(np.array([a]))[0] == b, (a, b)
+    # a value that float32 would round first (double rounding) is rounded once here
+    a = 1 + 2 ** -8 + 2 ** -30      # float32 -> 1 + 2^-8 -> bf16 1.0; exact -> 1 + 2^-7
+    assert ref.round_bf16(np.array([a]))[0] == 1 + 2 ** -7
+
+
+def _chain_problems(N, C1, K1, K2, L):
+    p1 = sd.conv1d_problem(N, C1, K1, L, 3, 1, 1)
+    p2 = sd.conv1d_problem(N, K1, K2, L, 3, 2, 1)
+    return p1, p2
+
+
+@pytest.mark.parametrize("gelu", [False, True])
+def test_chain_delta_filters_closed_form(gelu):
+    """conv1 copies input channel k mod C1 (centre tap), conv2 copies channel
+    k (centre tap, stride 2): y[n, o, k] = act(round_bf16(act(x[n, 2o, k mod C1])))
+    with act = GELU or identity."""
+    N, C1, K1, L = 2, 16, 48, 37
+    p1, p2 = _chain_problems(N, C1, K1, K1, L)
+    rng = np.random.Generator(np.random.PCG64(72))
+    x = sd.round_bf16(rng.uniform(-4, 4, ref.shapes(p1)[0]).astype(np.float32))
+    w1 = np.zeros(ref.shapes(p1)[1])
+    w2 = np.zeros(ref.shapes(p2)[1])
+    for k in range(K1):
+        w1[0, k, 0, 0, 1, k % C1] = 1.0
+        w2[0, k, 0, 0, 1, k] = 1.0
+    y, _, _ = ref.conv_chain(p1, p2, x, w1, None, w2, None, gelu)
+    act = (lambda t: 0.5 * t * np.vectorize(math.erfc)(-t / math.sqrt(2.0))) if gelu else (lambda t: t)
+    xs = x.astype(np.float64).reshape(N, L, C1)
+    Lo = ref.out_dims(p2)[2]
+    want = np.empty((N, Lo, K1))
+    for k in range(K1):
+        want[:, :, k] = act(ref.round_bf16(act(xs[:, 0:2 * Lo:2, k % C1])))
+    assert np.array_equal(y.reshape(N, Lo, K1), want)
+
+
+def test_chain_interior_equals_composed_kernel():
+    """Away from the borders (where the zero padding of h matters) the chain
+    with no activation is one 5-tap, stride-2 conv whose kernel is the
+    composition of the two: W[k, s, c] = sum_{t2+t1=s} sum_j w2[k,t2,j] w1[j,t1,c].
+    Integer inputs keep every value exact (h fits bf16)."""
+    N, C1, K1, K2, L = 2, 5, 7, 6, 40
+    p1, p2 = _chain_problems(N, C1, K1, K2, L)
+    rng = np.random.Generator(np.random.PCG64(73))
+    x = rng.integers(-2, 3, ref.shapes(p1)[0]).astype(np.float64)
+    w1 = rng.integers(-1, 2, ref.shapes(p1)[1]).astype(np.float64)
+    w2 = rng.integers(-1, 2, ref.shapes(p2)[1]).astype(np.float64)
+    y, _, _ = ref.conv_chain(p1, p2, x, w1, None, w2, None, False)
+    W1 = w1.reshape(K1, 3, C1)
+    W2 = w2.reshape(K2, 3, K1)
+    Wc = np.zeros((K2, 5, C1))
+    for t2 in range(3):
+        for t1 in range(3):
+            Wc[:, t2 + t1, :] += W2[:, t2, :] @ W1[:, t1, :]
+    xs = x.reshape(N, L, C1)
+    Lo = ref.out_dims(p2)[2]
+    ys = y.reshape(N, Lo, K2)
+    for o in range(1, Lo - 1):          # h positions 2o-1 .. 2o+1 are all inside [1, L-2]
+        win = xs[:, 2 * o - 2:2 * o + 3, :]              # x positions 2o-2 .. 2o+2
+        want = np.einsum("nsc,ksc->nk", win, Wc)
+        assert np.array_equal(ys[:, o, :], want), o
+
+
+def test_chain_points_equal_full_chain():
+    N, C1, K1, K2, L = 2, 16, 24, 8, 29
+    p1, p2 = _chain_problems(N, C1, K1, K2, L)
+    rng = np.random.Generator(np.random.PCG64(74))
+    x = rng.standard_normal(ref.shapes(p1)[0])
+    w1 = rng.standard_normal(ref.shapes(p1)[1]) * 0.2
+    b1 = rng.standard_normal(ref.shapes(p1)[2]) * 0.1
+    w2 = rng.standard_normal(ref.shapes(p2)[1]) * 0.2
+    b2 = rng.standard_normal(ref.shapes(p2)[2]) * 0.1
+    y, a2, c = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, True)
+    idx = np.array([0, 1, 7, 100, y.size - 1], dtype=np.int64)
+    yp, a2p, cp = ref.conv_chain_points(p1, p2, x, w1, b1, w2, b2, True, idx)
+    assert np.array_equal(yp, y.ravel()[idx])
+    assert np.allclose(a2p, a2.ravel()[idx], rtol=1e-13, atol=0)
+    assert np.allclose(cp, c.ravel()[idx], rtol=1e-13, atol=0)
+
+
+def test_chain_bound_accepts_a_float32_chain_and_rejects_a_perturbation():
+    """A float32 re-implementation of the chain (float32 sums, bf16-rounded
+    h) stays within check_chain's bound; adding 3x the bound fails it."""
+    N, C1, K1, K2, L = 1, 16, 32, 16, 33
+    p1, p2 = _chain_problems(N, C1, K1, K2, L)
+    rng = np.random.Generator(np.random.PCG64(75))
+    x = sd.round_bf16(rng.uniform(-1, 1, ref.shapes(p1)[0]).astype(np.float32))
+    w1 = sd.round_bf16((rng.standard_normal(ref.shapes(p1)[1]) * 0.1).astype(np.float32))
+    b1 = sd.round_bf16((rng.standard_normal(ref.shapes(p1)[2]) * 0.02).astype(np.float32))
+    w2 = sd.round_bf16((rng.standard_normal(ref.shapes(p2)[1]) * 0.1).astype(np.float32))
+    b2 = sd.round_bf16((rng.standard_normal(ref.shapes(p2)[2]) * 0.02).astype(np.float32))
+    y, a2, c = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, True)
+
+    def f32_conv(xx, ww, bb, Cin, Kout, Lin, stride):
+        xs = np.zeros((Lin + 2, Cin), np.float32)
+        xs[1:-1] = xx.reshape(Lin, Cin)
+        Lout = (Lin - 1) // stride + 1
+        out = np.zeros((Lout, Kout), np.float32)
+        Wt = ww.reshape(Kout, 3, Cin).astype(np.float32)
+        for o in range(Lout):
+            acc = bb.astype(np.float32).copy()
+            for t in range(3):
+                acc = acc + (xs[o * stride + t][None, :] * Wt[:, t, :]).sum(axis=1, dtype=np.float32)
+            out[o] = acc
+        g = 0.5 * out.astype(np.float64) * np.vectorize(math.erfc)(-out.astype(np.float64) / math.sqrt(2.0))
+        return g.astype(np.float32)
+
+    h = f32_conv(x, w1, b1, C1, K1, L, 1)
+    h = sd.round_bf16(h)
+    g = f32_conv(h, w2, b2, K1, K2, L, 2).astype(np.float64).ravel()
+    st = check.check_chain(g, y, a2, c, p1, p2, True)
+    assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
+    for i in (0, g.size // 2, g.size - 1):
+        bad = g.copy()
+        bad[i] = y.ravel()[i] + 3 * st["limit"][i]
+        assert not check.check_chain(bad, y, a2, c, p1, p2, True)["ok"]
