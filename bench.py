@@ -126,6 +126,8 @@ def main():
                     help="record the dominant kernel's start/stop events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run a two-conv frontend workload as one fused kernel (conv_chain_*)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes --steps times")
     args = ap.parse_args()
@@ -139,7 +141,7 @@ def main():
     import numpy as np
     import torch
     import synthdata as sd
-    from convolution_forward_implicit_amd import ConvFwd
+    from convolution_forward_implicit_amd import ConvFwd, ConvChain
 
     if args.copy_bytes:
         a = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
@@ -160,22 +162,46 @@ def main():
 
     convs, ws, bs, outs = [], [], [], []
     x0 = up(W["x"])
-    for li, (p, hb, ge) in enumerate(W["layers"]):
-        c = ConvFwd(p, dt, hb, ge)
-        convs.append(c)
-        ws.append(up(W["w"][li]))
-        bs.append(up(W["b"][li]) if hb else None)
-        outs.append(torch.empty(c.y_shape, dtype=tdt, device=dev))
-    flops = [c.useful_flop() for c in convs]
-    dom = int(np.argmax(flops))
     stream = torch.cuda.current_stream(dev)
+    esz = 4 if dt == "f32" else 2
+    if args.fused:
+        if len(W["layers"]) != 2:
+            print("bench.py: --fused needs a two-conv workload", file=sys.stderr)
+            sys.exit(2)
+        (p1, hb, ge), (p2, _, _) = W["layers"]
+        chain = ConvChain(p1, p2, dt, hb, ge)
+        w1, w2 = up(W["w"][0]), up(W["w"][1])
+        b1, b2 = (up(W["b"][0]), up(W["b"][1])) if hb else (None, None)
+        y = torch.empty(chain.y_shape, dtype=tdt, device=dev)
+        convs = [chain]
+        flops = [chain.useful_flop()]
+        dom = 0
+        dom_alg_bytes = esz * (int(np.prod(chain.x_shape)) + int(np.prod(chain.w1_shape)) +
+                               int(np.prod(chain.w2_shape)) + (2 * int(np.prod(chain.b_shape)) if hb else 0) +
+                               int(np.prod(chain.y_shape)))
 
-    def step(ev=None, i=0):
-        x = x0
-        for li, c in enumerate(convs):
-            kev = (ev[0][i], ev[1][i]) if ev is not None and li == dom else None
-            c(x, ws[li], bs[li], out=outs[li], stream=stream, events=kev)
-            x = outs[li]
+        def step(ev=None, i=0):
+            kev = (ev[0][i], ev[1][i]) if ev is not None else None
+            chain(x0, w1, b1, w2, b2, out=y, stream=stream, events=kev)
+    else:
+        for li, (p, hb, ge) in enumerate(W["layers"]):
+            c = ConvFwd(p, dt, hb, ge)
+            convs.append(c)
+            ws.append(up(W["w"][li]))
+            bs.append(up(W["b"][li]) if hb else None)
+            outs.append(torch.empty(c.y_shape, dtype=tdt, device=dev))
+        flops = [c.useful_flop() for c in convs]
+        dom = int(np.argmax(flops))
+        dom_alg_bytes = esz * (int(np.prod(convs[dom].x_shape)) + int(np.prod(convs[dom].w_shape)) +
+                               (int(np.prod(convs[dom].b_shape)) if convs[dom].has_bias else 0) +
+                               int(np.prod(convs[dom].y_shape)))
+
+        def step(ev=None, i=0):
+            x = x0
+            for li, c in enumerate(convs):
+                kev = (ev[0][i], ev[1][i]) if ev is not None and li == dom else None
+                c(x, ws[li], bs[li], out=outs[li], stream=stream, events=kev)
+                x = outs[li]
 
     for _ in range(args.warmup):
         step()
@@ -208,13 +234,10 @@ def main():
     total_flop = float(sum(flops))
     value = total_flop / (ms_step * 1e-3) / 1e12
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
-    esz = 4 if dt == "f32" else 2
-    alg_bytes = esz * (int(np.prod(convs[dom].x_shape)) + int(np.prod(convs[dom].w_shape)) +
-                       (int(np.prod(convs[dom].b_shape)) if convs[dom].has_bias else 0) +
-                       int(np.prod(convs[dom].y_shape)))
+    alg_bytes = dom_alg_bytes
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dt],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4),
-            "traffic": recorded_traffic(args.workload, dom, alg_bytes),
+            "traffic": recorded_traffic(args.workload + ("_fused" if args.fused else ""), dom, alg_bytes),
             "kernel": "layer %d: %s" % (dom + 1, convs[dom].describe()),
             "kernel_ms": round(dom_ms, 5), "kernel_launches_timed": NE, "algorithmic_bytes": alg_bytes,
             "hbm_GBs_algorithmic": round(alg_bytes / (dom_ms * 1e-3) / 1e9, 1)}
@@ -229,7 +252,7 @@ def main():
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": W["layers"][0][0]["N"],
+        "config": {"workload": args.workload, "fused": bool(args.fused), "batch": W["layers"][0][0]["N"],
                    "layers": [c.describe() for c in convs], "useful_gflop_per_step": round(total_flop / 1e9, 4),
                    "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU"},
         "roofline": roof, "cpu_baseline": cpu,

@@ -12,11 +12,14 @@ device memory and streams:
 A problem is a dict {"N", "G", "C", "K", "in": (D, H, W), "filt": (Z, Y, X),
 "stride", "pad", "dil"} (C and K per group); a 1-D convolution has
 D = H = 1, a 2-D one D = 1.
+
+ConvChain(first, second, "bf16", has_bias, gelu) runs two 1-D convs back to
+back in one kernel (the conv frontend), the intermediate kept on chip.
 """
 from . import capi
 from .capi import ConvError  # noqa: F401
 
-__all__ = ["ConvFwd", "ConvError", "capi", "desc_from_problem"]
+__all__ = ["ConvFwd", "ConvChain", "ConvError", "capi", "desc_from_problem"]
 
 
 def _ndim(p):
@@ -112,4 +115,86 @@ class ConvFwd:
         else:
             capi.conv_fwd_run_events(self._plan, xp, wp, bp, yp, s.cuda_stream,
                                      events[0].cuda_event, events[1].cuda_event)
+        return out
+
+
+class ConvChain:
+    """A fused two-conv 1-D plan (conv_chain_create): y = act(conv2(h) + b2),
+    h = round_bf16(act(conv1(x) + b1)).  Raises ConvError (UNSUPPORTED) for a
+    chain outside the supported set (see include/convfwd.h)."""
+
+    def __init__(self, first, second, dtype="bf16", has_bias=False, gelu=False):
+        self.first, self.second = dict(first), dict(second)
+        self.dtype = dtype
+        self.has_bias = bool(has_bias)
+        self.gelu = bool(gelu)
+        self._plan = capi.conv_chain_create(desc_from_problem(first, dtype, has_bias, gelu),
+                                            desc_from_problem(second, dtype, has_bias, gelu))
+        p1, p2 = self.first, self.second
+        self.x_shape = (p1["N"],) + tuple(p1["in"]) + (p1["G"], p1["C"])
+        self.w1_shape = (p1["G"], p1["K"]) + tuple(p1["filt"]) + (p1["C"],)
+        self.w2_shape = (p2["G"], p2["K"]) + tuple(p2["filt"]) + (p2["C"],)
+        self.b_shape = (p1["G"], p1["K"])
+        Lo = (p2["in"][2] + 2 * p2["pad"][2] - p2["dil"][2] * (p2["filt"][2] - 1) - 1) // p2["stride"][2] + 1
+        self.y_shape = (p2["N"], 1, 1, Lo, p2["G"], p2["K"])
+
+    def useful_flop(self):
+        """Both convs' 2 * multiply-adds, counting padded taps."""
+        n = 0
+        for p in (self.first, self.second):
+            o = (p["in"][2] + 2 * p["pad"][2] - p["dil"][2] * (p["filt"][2] - 1) - 1) // p["stride"][2] + 1
+            n += 2 * p["N"] * p["K"] * p["C"] * p["filt"][2] * o
+        return n
+
+    def describe(self):
+        return capi.conv_chain_describe(self._plan)
+
+    def close(self):
+        if getattr(self, "_plan", None):
+            capi.conv_chain_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _tensor(self, t, shape, name, torch):
+        if t.device.type != "cuda":
+            raise ValueError("%s must be a cuda tensor" % name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be torch.bfloat16, got %s" % (name, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        n = 1
+        for s in shape:
+            n *= s
+        if t.numel() != n:
+            raise ValueError("%s has %d elements, expected shape %r" % (name, t.numel(), shape))
+        return t.data_ptr()
+
+    def __call__(self, x, w1, b1, w2, b2, out=None, stream=None, events=None):
+        import torch
+        xp = self._tensor(x, self.x_shape, "x", torch)
+        w1p = self._tensor(w1, self.w1_shape, "w1", torch)
+        w2p = self._tensor(w2, self.w2_shape, "w2", torch)
+        if self.has_bias:
+            if b1 is None or b2 is None:
+                raise ValueError("this chain has biases")
+            b1p = self._tensor(b1, self.b_shape, "b1", torch)
+            b2p = self._tensor(b2, self.b_shape, "b2", torch)
+        else:
+            if b1 is not None or b2 is not None:
+                raise ValueError("this chain has no bias")
+            b1p = b2p = None
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
+        yp = self._tensor(out, self.y_shape, "out", torch)
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        if events is None:
+            capi.conv_chain_run(self._plan, xp, w1p, b1p, w2p, b2p, yp, s.cuda_stream)
+        else:
+            capi.conv_chain_run_events(self._plan, xp, w1p, b1p, w2p, b2p, yp, s.cuda_stream,
+                                       events[0].cuda_event, events[1].cuda_event)
         return out

@@ -26,7 +26,9 @@ STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTE
 
 EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims",
             "conv_fwd_run", "conv_fwd_run_events", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
-            "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error"]
+            "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error",
+            "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
+            "conv_chain_describe"]
 
 
 class conv_fwd_desc_t(ctypes.Structure):
@@ -81,6 +83,16 @@ def lib():
         L.conv_fwd_config_dtype.restype = ctypes.c_int32
         L.conv_fwd_last_error.argtypes = []
         L.conv_fwd_last_error.restype = ctypes.c_char_p
+        L.conv_chain_create.argtypes = [D, D, ctypes.POINTER(P)]
+        L.conv_chain_create.restype = ctypes.c_int
+        L.conv_chain_run.argtypes = [P] * 8
+        L.conv_chain_run.restype = ctypes.c_int
+        L.conv_chain_run_events.argtypes = [P] * 10
+        L.conv_chain_run_events.restype = ctypes.c_int
+        L.conv_chain_destroy.argtypes = [P]
+        L.conv_chain_destroy.restype = None
+        L.conv_chain_describe.argtypes = [P]
+        L.conv_chain_describe.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -149,6 +161,28 @@ def conv_fwd_config_name(config):
 
 def conv_fwd_config_dtype(config):
     return int(lib().conv_fwd_config_dtype(int(config)))
+
+
+def conv_chain_create(first, second):
+    plan = ctypes.c_void_p()
+    _check(lib().conv_chain_create(ctypes.byref(first), ctypes.byref(second), ctypes.byref(plan)))
+    return plan.value
+
+
+def conv_chain_run(plan, x, w1, b1, w2, b2, y, stream=0):
+    _check(lib().conv_chain_run(plan, x, w1, b1, w2, b2, y, stream))
+
+
+def conv_chain_run_events(plan, x, w1, b1, w2, b2, y, stream=0, start_event=None, stop_event=None):
+    _check(lib().conv_chain_run_events(plan, x, w1, b1, w2, b2, y, stream, start_event, stop_event))
+
+
+def conv_chain_destroy(plan):
+    lib().conv_chain_destroy(plan)
+
+
+def conv_chain_describe(plan):
+    return lib().conv_chain_describe(plan).decode()
 
 
 def conv_fwd_last_error():

@@ -25,6 +25,7 @@
 #include "igemm_kernel.h"
 #include "igemm_dma.h"
 #include "patch_kernel.h"
+#include "chain_kernel.h"
 
 namespace convfwd {
 namespace {
@@ -273,6 +274,14 @@ int device_cu_count()
 }  // namespace convfwd
 
 using namespace convfwd;
+
+struct conv_chain_plan {
+    conv_fwd_desc_t first, second;
+    int64_t x_elems, w1_elems, w2_elems, b_elems, y_elems;
+    ChainParams cp;  // pointers filled per run
+    int grid;
+    char text[256];
+};
 
 struct conv_fwd_plan {
     conv_fwd_desc_t desc;
@@ -597,4 +606,111 @@ void conv_fwd_destroy(conv_fwd_plan_t *plan) { delete plan; }
 
 const char *conv_fwd_describe(const conv_fwd_plan_t *plan) { return plan ? plan->text : ""; }
 
-}  // extern "C"
+conv_status_t conv_chain_create(const conv_fwd_desc_t *first, const conv_fwd_desc_t *second,
+                                conv_chain_plan_t **plan)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    *plan = nullptr;
+    int64_t o1[3], o2[3];
+    conv_status_t st = validate(first, o1);
+    if (st != CONV_OK) return st;
+    st = validate(second, o2);
+    if (st != CONV_OK) return st;
+    const conv_fwd_desc_t &a = *first, &b = *second;
+    using S = ChainShape;
+    if (a.ndim != 1 || b.ndim != 1 || a.dtype != CONV_DT_BF16 || b.dtype != CONV_DT_BF16 || a.G != 1 || b.G != 1)
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: both convs must be 1-D, bf16, one group");
+    if (b.N != a.N || b.C != a.K || b.in[2] != o1[2])
+        return fail(CONV_ERR_INVALID_ARG, "fused chain: the second conv must read the first one's output "
+                                          "(same N, C2 == K1, input length == first output length)");
+    if (a.filt[2] != 3 || a.stride[2] != 1 || a.pad[2] != 1 || a.dilation[2] != 1 || b.filt[2] != 3 ||
+        b.stride[2] != 2 || b.pad[2] != 1 || b.dilation[2] != 1)
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: needs conv1 k3 s1 p1 and conv2 k3 s2 p1 (no dilation)");
+    if (a.K != S::K || b.K != S::K)
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: needs %d channels after each conv", S::K);
+    if (a.C % 16 != 0 || a.C > S::C1MAX)
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: needs C1 a multiple of 16 and at most %d (C1 = %lld)",
+                    S::C1MAX, (long long)a.C);
+    if (a.has_bias != b.has_bias || a.gelu != b.gelu)
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: both convs must agree on bias and GELU");
+    conv_chain_plan *pl = new (std::nothrow) conv_chain_plan();
+    if (!pl) return fail(CONV_ERR_NOMEM, "plan allocation failed");
+    pl->first = a;
+    pl->second = b;
+    pl->x_elems = a.N * a.in[2] * a.C;
+    pl->w1_elems = a.K * 3 * a.C;
+    pl->w2_elems = b.K * 3 * b.C;
+    pl->b_elems = a.has_bias ? S::K : 0;
+    pl->y_elems = b.N * o2[2] * b.K;
+    if (pl->x_elems * 2 >= (int64_t(1) << 31) || pl->y_elems * 2 >= (int64_t(1) << 31)) {
+        delete pl;
+        return fail(CONV_ERR_UNSUPPORTED, "fused chain: x and y must be below 2 GiB");
+    }
+    ChainParams &cp = pl->cp;
+    cp.N = (int)a.N;
+    cp.L = (int)a.in[2];
+    cp.C1 = (int)a.C;
+    cp.Lo = (int)o2[2];
+    cp.tiles = (cp.Lo + S::TO - 1) / S::TO;
+    cp.x_bytes = (uint32_t)(pl->x_elems * 2);
+    cp.w1_bytes = (uint32_t)(pl->w1_elems * 2);
+    cp.w2_bytes = (uint32_t)(pl->w2_elems * 2);
+    pl->grid = (int)(a.N * cp.tiles);
+    snprintf(pl->text, sizeof(pl->text),
+             "chain bf16 N=%d L=%d C1=%d -> %d -> %d Lo=%d grid=%d (%d outputs per workgroup) lds=%dB%s%s",
+             cp.N, cp.L, cp.C1, S::K, S::K, cp.Lo, pl->grid, S::TO, S::LDS_BYTES, a.has_bias ? " bias" : "",
+             a.gelu ? " gelu" : "");
+    if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
+    *plan = pl;
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_run_events(const conv_chain_plan_t *plan, const void *x, const void *w1, const void *b1,
+                                    const void *w2, const void *b2, void *y, void *stream, void *start_event,
+                                    void *stop_event)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    const bool hb = plan->first.has_bias != 0;
+    if (hb && (!b1 || !b2)) return fail(CONV_ERR_INVALID_ARG, "plan has biases but b1 or b2 is NULL");
+    if (!hb && (b1 || b2)) return fail(CONV_ERR_INVALID_ARG, "plan has no bias but b1 or b2 is not NULL");
+    if (!w1 || !w2) return fail(CONV_ERR_INVALID_ARG, "w1 or w2 is NULL");
+    if (plan->y_elems == 0) return CONV_OK;
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "x or y is NULL");
+    if (((uintptr_t)x | (uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)y) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "x, w1, w2 and y must be 16-byte aligned");
+    if (((uintptr_t)b1 | (uintptr_t)b2) & 1u) return fail(CONV_ERR_INVALID_ARG, "b1 and b2 must be 2-byte aligned");
+    const int64_t yb = plan->y_elems * 2;
+    if (overlaps(y, yb, x, plan->x_elems * 2) || overlaps(y, yb, w1, plan->w1_elems * 2) ||
+        overlaps(y, yb, w2, plan->w2_elems * 2) || overlaps(y, yb, b1, plan->b_elems * 2) ||
+        overlaps(y, yb, b2, plan->b_elems * 2))
+        return fail(CONV_ERR_INVALID_ARG, "y overlaps an input");
+    ChainParams cp = plan->cp;
+    cp.x = x; cp.w1 = w1; cp.b1 = b1; cp.w2 = w2; cp.b2 = b2; cp.y = y;
+    (void)hipGetLastError();
+    const dim3 g(plan->grid), blk(256);
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = (hipEvent_t)start_event, e1 = (hipEvent_t)stop_event;
+    if (hb && plan->first.gelu)
+        hipExtLaunchKernelGGL((chain_kernel<true, true>), g, blk, 0, s, e0, e1, 0, cp);
+    else if (hb)
+        hipExtLaunchKernelGGL((chain_kernel<true, false>), g, blk, 0, s, e0, e1, 0, cp);
+    else if (plan->first.gelu)
+        hipExtLaunchKernelGGL((chain_kernel<false, true>), g, blk, 0, s, e0, e1, 0, cp);
+    else
+        hipExtLaunchKernelGGL((chain_kernel<false, false>), g, blk, 0, s, e0, e1, 0, cp);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_run(const conv_chain_plan_t *plan, const void *x, const void *w1, const void *b1,
+                             const void *w2, const void *b2, void *y, void *stream)
+{
+    return conv_chain_run_events(plan, x, w1, b1, w2, b2, y, stream, nullptr, nullptr);
+}
+
+void conv_chain_destroy(conv_chain_plan_t *plan) { delete plan; }
+
+const char *conv_chain_describe(const conv_chain_plan_t *plan) { return plan ? plan->text : ""; }
+
+}  // extern "C\"

@@ -137,6 +137,52 @@ int32_t conv_fwd_num_configs(void);
 const char *conv_fwd_config_name(int32_t config);
 int32_t conv_fwd_config_dtype(int32_t config);
 
+/* ---- Fused two-conv 1-D frontend -----------------------------------------
+ * The conv frontend of the ExecuTorch conv1d issue (section "Describe the
+ * bug", the table that splits it into conv1 + GELU + conv2 + GELU), run as
+ * one kernel whose intermediate never leaves the chip:
+ *
+ *   h = round_bf16(act(conv1(x) + b1)),   y = act(conv2(h) + b2)
+ *
+ * conv1 and conv2 follow conv_fwd (cross-correlation, zero padding, act =
+ * identity or erf-GELU, bf16 in and out, fp32 sums); h has the call's dtype
+ * (bf16), as the unfused chain would store it.  Supported: both 1-D, bf16,
+ * G = 1; conv1 C1 -> 384 channels, kernel 3, stride 1, pad 1, C1 a
+ * multiple of 16 and at most 352; conv2 384 -> 384, kernel 3, stride 2,
+ * pad 1; no dilation; both with the same bias and GELU flags; x and y below
+ * 2 GiB.  Layouts as conv_fwd with ndim = 1: x N x L x C1, w1 384 x 3 x C1,
+ * w2 384 x 3 x 384, b1 and b2 384, y N x Lo x 384 (Lo = (L - 1) / 2 + 1).
+ * Ownership, threading and asynchrony as conv_fwd. */
+typedef struct conv_chain_plan conv_chain_plan_t;   /* opaque */
+
+/* Validates both descriptors (each as conv_fwd_create would) and checks that
+ * they form a supported chain.
+ *   CONV_ERR_INVALID_ARG : NULL pointers, an invalid descriptor, or a second
+ *                          conv that does not read the first one's output
+ *                          (N, C2 == K1, input length == first output length).
+ *   CONV_ERR_UNSUPPORTED : a valid chain outside the supported set above.
+ *   CONV_ERR_NOMEM       : plan allocation failed. */
+conv_status_t conv_chain_create(const conv_fwd_desc_t *first, const conv_fwd_desc_t *second,
+                                conv_chain_plan_t **plan);
+
+/* Enqueues the fused chain on `stream`.  x, w1, w2, y: device pointers,
+ * 16-byte aligned; b1, b2: device pointers (NULL iff the plan has no bias).
+ * y must not overlap an input.  Errors as conv_fwd_run. */
+conv_status_t conv_chain_run(const conv_chain_plan_t *plan, const void *x, const void *w1, const void *b1,
+                             const void *w2, const void *b2, void *y, void *stream);
+
+/* As conv_chain_run, recording start_event / stop_event (may be NULL) when
+ * the kernel starts and ends, as conv_fwd_run_events does. */
+conv_status_t conv_chain_run_events(const conv_chain_plan_t *plan, const void *x, const void *w1,
+                                    const void *b1, const void *w2, const void *b2, void *y, void *stream,
+                                    void *start_event, void *stop_event);
+
+/* Frees a chain plan (NULL is a no-op). */
+void conv_chain_destroy(conv_chain_plan_t *plan);
+
+/* Description of the chain plan; owned by the plan.  "" for NULL. */
+const char *conv_chain_describe(const conv_chain_plan_t *plan);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *conv_fwd_last_error(void);
 

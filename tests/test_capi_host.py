@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv_fwd_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv_(?:fwd|chain)_\w+)\s*\(", text)))
 
 
 def test_header_declares_what_binding_expects():
@@ -247,3 +247,61 @@ def test_tuning_records_match_sweep_and_configs(tmp_path):
         name = l.split('"')[1]
         assert name in dtype_of, name
         assert dtype_of[name] == int(l.strip()[1]), l
+
+
+# --------------------------------------------------------------------------
+# Fused two-conv chain: plan-time validation (no GPU work)
+def _chain_descs(N=2, C1=80, L=300, K1=384, K2=384, k1=3, s1=1, k2=3, s2=2, dtype="bf16", hb=True, ge=True,
+                 hb2=None, ge2=None, L2=None):
+    p1 = sd.conv1d_problem(N, C1, K1, L, k1, s1, k1 // 2)
+    o1 = ref.out_dims(p1)[2]
+    p2 = sd.conv1d_problem(N, K1, K2, o1 if L2 is None else L2, k2, s2, k2 // 2)
+    return (desc_from_problem(p1, dtype, hb, ge),
+            desc_from_problem(p2, dtype, hb if hb2 is None else hb2, ge if ge2 is None else ge2))
+
+
+def test_chain_create_accepts_the_frontend_and_describes_it():
+    a, b = _chain_descs()
+    plan = capi.conv_chain_create(a, b)
+    try:
+        text = capi.conv_chain_describe(plan)
+        assert "chain bf16" in text and "C1=80" in text and "Lo=150" in text and "gelu" in text
+    finally:
+        capi.conv_chain_destroy(plan)
+    capi.conv_chain_destroy(None)
+    assert capi.conv_chain_describe(None) == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype="f32"), capi.CONV_ERR_UNSUPPORTED),
+    (dict(C1=72), capi.CONV_ERR_UNSUPPORTED),          # not a multiple of 16
+    (dict(C1=368), capi.CONV_ERR_UNSUPPORTED),         # above the input-patch limit
+    (dict(K1=256), capi.CONV_ERR_UNSUPPORTED),
+    (dict(K2=256), capi.CONV_ERR_UNSUPPORTED),
+    (dict(k1=5), capi.CONV_ERR_UNSUPPORTED),
+    (dict(s2=1), capi.CONV_ERR_UNSUPPORTED),
+    (dict(ge2=False), capi.CONV_ERR_UNSUPPORTED),
+    (dict(hb2=False), capi.CONV_ERR_UNSUPPORTED),
+    (dict(L2=299), capi.CONV_ERR_INVALID_ARG),         # second conv does not read the first's output
+])
+def test_chain_create_rejects(kw, status):
+    a, b = _chain_descs(**kw)
+    with pytest.raises(ConvError) as e:
+        capi.conv_chain_create(a, b)
+    assert e.value.status == status, e.value.message
+
+
+def test_chain_run_rejects_bad_arguments_before_launching():
+    a, b = _chain_descs()
+    plan = capi.conv_chain_create(a, b)
+    try:
+        with pytest.raises(ConvError):
+            capi.conv_chain_run(plan, 16, 16, None, 16, None, 4096)     # plan has biases
+        with pytest.raises(ConvError):
+            capi.conv_chain_run(plan, 16, None, 32, 16, 32, 4096)       # w1 NULL
+        with pytest.raises(ConvError):
+            capi.conv_chain_run(plan, 8, 16, 32, 16, 32, 4096)          # misaligned x
+        with pytest.raises(ConvError):
+            capi.conv_chain_run(None, 16, 16, 32, 16, 32, 4096)
+    finally:
+        capi.conv_chain_destroy(plan)

@@ -267,3 +267,72 @@ def test_repeat_runs_bitwise_identical(dev):
     y2 = c(to_dev(W["x"], "bf16", dev), to_dev(W["w"][0], "bf16", dev))
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# Fused two-conv frontend (conv_chain_*): the intermediate never leaves the
+# chip, so the oracle rounds its own exact intermediate to bf16
+# (oracle.ref.conv_chain) and the bound carries the possible one-step
+# difference of that rounding through conv2 (oracle.check.check_chain).
+def _chain(N, L, C1=80):
+    p1 = sd.conv1d_problem(N, C1, 384, L, 3, 1, 1)
+    p2 = sd.conv1d_problem(N, 384, 384, L, 3, 2, 1)
+    return p1, p2
+
+
+def run_chain(dev, p1, p2, x, w1, b1, w2, b2, gelu):
+    from convolution_forward_implicit_amd import ConvChain
+    c = ConvChain(p1, p2, "bf16", b1 is not None, gelu)
+    print("case: chain", p1, "gelu" if gelu else "", c.describe(), flush=True)
+    t = lambda a: None if a is None else to_dev(a, "bf16", dev)
+    y = c(t(x), t(w1), t(b1), t(w2), t(b2))
+    torch.cuda.synchronize()
+    return y, c
+
+
+@pytest.mark.parametrize("N,L,C1", [(2, 300, 80), (3, 1001, 80), (1, 130, 16), (2, 257, 352)])
+def test_chain_integer_bit_exact(dev, N, L, C1):
+    """Integer inputs: conv1's fp32 sums are exact, so the device's bf16 h is
+    the oracle's rounding of the exact h, conv2's sums of those bf16 values
+    are exact too, and the bf16 output has one correct value."""
+    p1, p2 = _chain(N, L, C1)
+    x, w1, b1 = sd.random_inputs(p1, "bf16", 81, True, kind="int")
+    _, w2, b2 = sd.random_inputs(p2, "bf16", 82, True, kind="int")
+    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, False)
+    r, _, _ = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, False)
+    assert np.array_equal(bits(y).ravel(), check.round_to_bf16_bits(r).ravel())
+
+
+@pytest.mark.parametrize("N,L", [(2, 301), (1, 64), (2, 127)])
+def test_chain_seeded_float_parity(dev, N, L):
+    p1, p2 = _chain(N, L)
+    x, w1, b1 = sd.random_inputs(p1, "bf16", 83, True)
+    _, w2, b2 = sd.random_inputs(p2, "bf16", 84, True)
+    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, True)
+    r, a2, cy = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, True)
+    st = check.check_chain(host(y), r, a2, cy, p1, p2, True)
+    print("parity:", {k: v for k, v in st.items() if k != "limit"}, flush=True)
+    assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
+
+
+def test_chain_workload_full_size_sampled(dev):
+    """The batch-32 bf16 frontend at full size, in the launch the benchmark
+    times with --fused: 4000 random outputs plus borders against the oracle."""
+    W = sd.workload(3)
+    (p1, _, _), (p2, _, _) = W["layers"]
+    y, _ = run_chain(dev, p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True)
+    idx = sample_indices(p2, 4000, 85)
+    r, a2, cy = ref.conv_chain_points(p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True, idx)
+    st = check.check_chain(host(y).ravel()[idx], r, a2, cy, p1, p2, True)
+    print("parity:", {k: v for k, v in st.items() if k != "limit"}, flush=True)
+    assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
+
+
+def test_chain_empty_batch(dev):
+    from convolution_forward_implicit_amd import ConvChain
+    p1, p2 = _chain(0, 64)
+    c = ConvChain(p1, p2, "bf16", False, False)
+    e = lambda s: torch.empty(s, dtype=torch.bfloat16, device=dev)
+    y = e(c.y_shape)
+    assert c(e(c.x_shape), e(c.w1_shape), None, e(c.w2_shape), None, out=y) is y
+    torch.cuda.synchronize()
