@@ -127,7 +127,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--fused", action="store_true",
-                    help="run a two-conv frontend workload as one fused kernel (conv_chain_*)")
+                    help="run a two-conv frontend workload as one fused kernel from prepacked weights "
+                         "(conv_chain_pack_weights once, then conv_chain_run_packed per step)")
+    ap.add_argument("--fused-natural", action="store_true",
+                    help="run a two-conv frontend workload as one fused kernel from the natural weights "
+                         "(conv_chain_run)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes --steps times")
     args = ap.parse_args()
@@ -164,7 +168,9 @@ def main():
     x0 = up(W["x"])
     stream = torch.cuda.current_stream(dev)
     esz = 4 if dt == "f32" else 2
-    if args.fused:
+    fused = args.fused or args.fused_natural
+    prepack = None
+    if fused:
         if len(W["layers"]) != 2:
             print("bench.py: --fused needs a two-conv workload", file=sys.stderr)
             sys.exit(2)
@@ -180,9 +186,25 @@ def main():
                                int(np.prod(chain.w2_shape)) + (2 * int(np.prod(chain.b_shape)) if hb else 0) +
                                int(np.prod(chain.y_shape)))
 
-        def step(ev=None, i=0):
-            kev = (ev[0][i], ev[1][i]) if ev is not None else None
-            chain(x0, w1, b1, w2, b2, out=y, stream=stream, events=kev)
+        if args.fused:
+            # weights are constant across steps: prepack once, as a model load would
+            wp = chain.pack(w1, w2, stream=stream)
+            pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            torch.cuda.synchronize()
+            pe[0].record(stream)
+            chain.pack(w1, w2, out=wp, stream=stream)
+            pe[1].record(stream)
+            torch.cuda.synchronize()
+            prepack = {"ms": round(pe[0].elapsed_time(pe[1]), 5), "bytes": int(wp.numel()),
+                       "when": "once, before the timed steps (weights are constant)"}
+
+            def step(ev=None, i=0):
+                kev = (ev[0][i], ev[1][i]) if ev is not None else None
+                chain.run_packed(x0, wp, b1, b2, out=y, stream=stream, events=kev)
+        else:
+            def step(ev=None, i=0):
+                kev = (ev[0][i], ev[1][i]) if ev is not None else None
+                chain(x0, w1, b1, w2, b2, out=y, stream=stream, events=kev)
     else:
         for li, (p, hb, ge) in enumerate(W["layers"]):
             c = ConvFwd(p, dt, hb, ge)
@@ -237,7 +259,8 @@ def main():
     alg_bytes = dom_alg_bytes
     roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dt],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dt], 4),
-            "traffic": recorded_traffic(args.workload + ("_fused" if args.fused else ""), dom, alg_bytes),
+            "traffic": recorded_traffic(args.workload + ("_fused" if args.fused else "_fused_natural" if args.fused_natural
+                                                         else ""), dom, alg_bytes),
             "kernel": "layer %d: %s" % (dom + 1, convs[dom].describe()),
             "kernel_ms": round(dom_ms, 5), "kernel_launches_timed": NE, "algorithmic_bytes": alg_bytes,
             "hbm_GBs_algorithmic": round(alg_bytes / (dom_ms * 1e-3) / 1e9, 1)}
@@ -252,9 +275,11 @@ def main():
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": args.workload, "fused": bool(args.fused), "batch": W["layers"][0][0]["N"],
+        "config": {"workload": args.workload, "fused": "prepacked" if args.fused else "natural" if args.fused_natural
+                   else False, "batch": W["layers"][0][0]["N"],
                    "layers": [c.describe() for c in convs], "useful_gflop_per_step": round(total_flop / 1e9, 4),
-                   "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU"},
+                   "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU",
+                   "weight_prepack": prepack},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -14,7 +14,9 @@ A problem is a dict {"N", "G", "C", "K", "in": (D, H, W), "filt": (Z, Y, X),
 D = H = 1, a 2-D one D = 1.
 
 ConvChain(first, second, "bf16", has_bias, gelu) runs two 1-D convs back to
-back in one kernel (the conv frontend), the intermediate kept on chip.
+back in one kernel (the conv frontend), the intermediate kept on chip;
+ConvChain.pack(w1, w2) prepacks the weights once and ConvChain.run_packed
+runs the chain from them.
 """
 from . import capi
 from .capi import ConvError  # noqa: F401
@@ -197,4 +199,51 @@ class ConvChain:
         else:
             capi.conv_chain_run_events(self._plan, xp, w1p, b1p, w2p, b2p, yp, s.cuda_stream,
                                        events[0].cuda_event, events[1].cuda_event)
+        return out
+
+    def packed_bytes(self):
+        """Size of the prepacked weights (ConvError UNSUPPORTED beyond the
+        prepacked kernel's channel limit)."""
+        return capi.conv_chain_packed_bytes(self._plan)
+
+    def pack(self, w1, w2, out=None, stream=None):
+        """Prepacked weights (a uint8 cuda tensor) from w1 and w2, enqueued on
+        `stream`; do it once and reuse the result for every run_packed."""
+        import torch
+        w1p = self._tensor(w1, self.w1_shape, "w1", torch)
+        w2p = self._tensor(w2, self.w2_shape, "w2", torch)
+        nbytes = self.packed_bytes()
+        if out is None:
+            out = torch.empty(nbytes, dtype=torch.uint8, device=w1.device)
+        if out.device.type != "cuda" or out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() != nbytes:
+            raise ValueError("packed must be a contiguous cuda uint8 tensor of %d bytes" % nbytes)
+        s = stream if stream is not None else torch.cuda.current_stream(w1.device)
+        capi.conv_chain_pack_weights(self._plan, w1p, w2p, out.data_ptr(), s.cuda_stream)
+        return out
+
+    def run_packed(self, x, packed, b1, b2, out=None, stream=None, events=None):
+        import torch
+        xp = self._tensor(x, self.x_shape, "x", torch)
+        if packed.device.type != "cuda" or packed.dtype != torch.uint8 or not packed.is_contiguous():
+            raise ValueError("packed must be a contiguous cuda uint8 tensor (from pack)")
+        if packed.numel() != self.packed_bytes():
+            raise ValueError("packed has %d bytes, expected %d" % (packed.numel(), self.packed_bytes()))
+        if self.has_bias:
+            if b1 is None or b2 is None:
+                raise ValueError("this chain has biases")
+            b1p = self._tensor(b1, self.b_shape, "b1", torch)
+            b2p = self._tensor(b2, self.b_shape, "b2", torch)
+        else:
+            if b1 is not None or b2 is not None:
+                raise ValueError("this chain has no bias")
+            b1p = b2p = None
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
+        yp = self._tensor(out, self.y_shape, "out", torch)
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        if events is None:
+            capi.conv_chain_run_packed(self._plan, xp, packed.data_ptr(), b1p, b2p, yp, s.cuda_stream)
+        else:
+            capi.conv_chain_run_packed_events(self._plan, xp, packed.data_ptr(), b1p, b2p, yp, s.cuda_stream,
+                                              events[0].cuda_event, events[1].cuda_event)
         return out

@@ -28,7 +28,8 @@ EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims
             "conv_fwd_run", "conv_fwd_run_events", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
             "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error",
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
-            "conv_chain_describe"]
+            "conv_chain_describe", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
+            "conv_chain_run_packed_events"]
 
 
 class conv_fwd_desc_t(ctypes.Structure):
@@ -93,6 +94,14 @@ def lib():
         L.conv_chain_destroy.restype = None
         L.conv_chain_describe.argtypes = [P]
         L.conv_chain_describe.restype = ctypes.c_char_p
+        L.conv_chain_packed_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_chain_packed_bytes.restype = ctypes.c_int
+        L.conv_chain_pack_weights.argtypes = [P] * 5
+        L.conv_chain_pack_weights.restype = ctypes.c_int
+        L.conv_chain_run_packed.argtypes = [P] * 7
+        L.conv_chain_run_packed.restype = ctypes.c_int
+        L.conv_chain_run_packed_events.argtypes = [P] * 9
+        L.conv_chain_run_packed_events.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -183,6 +192,24 @@ def conv_chain_destroy(plan):
 
 def conv_chain_describe(plan):
     return lib().conv_chain_describe(plan).decode()
+
+
+def conv_chain_packed_bytes(plan):
+    n = ctypes.c_int64()
+    _check(lib().conv_chain_packed_bytes(plan, ctypes.byref(n)))
+    return n.value
+
+
+def conv_chain_pack_weights(plan, w1, w2, packed, stream=0):
+    _check(lib().conv_chain_pack_weights(plan, w1, w2, packed, stream))
+
+
+def conv_chain_run_packed(plan, x, packed, b1, b2, y, stream=0):
+    _check(lib().conv_chain_run_packed(plan, x, packed, b1, b2, y, stream))
+
+
+def conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream=0, start_event=None, stop_event=None):
+    _check(lib().conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream, start_event, stop_event))
 
 
 def conv_fwd_last_error():

@@ -26,6 +26,7 @@
 #include "igemm_dma.h"
 #include "patch_kernel.h"
 #include "chain_kernel.h"
+#include "chain_packed.h"
 
 namespace convfwd {
 namespace {
@@ -280,7 +281,10 @@ struct conv_chain_plan {
     int64_t x_elems, w1_elems, w2_elems, b_elems, y_elems;
     ChainParams cp;  // pointers filled per run
     int grid;
-    char text[256];
+    ChainPackedParams pp;  // prepacked-weight kernel; pointers filled per run
+    int pgrid;
+    int64_t packed_bytes;   // 0: C1 beyond what the prepacked kernel supports
+    char text[320];
 };
 
 struct conv_fwd_plan {
@@ -656,10 +660,21 @@ conv_status_t conv_chain_create(const conv_fwd_desc_t *first, const conv_fwd_des
     cp.w1_bytes = (uint32_t)(pl->w1_elems * 2);
     cp.w2_bytes = (uint32_t)(pl->w2_elems * 2);
     pl->grid = (int)(a.N * cp.tiles);
+    using P = ChainPackedShape;
+    ChainPackedParams &pp = pl->pp;
+    pp.N = cp.N;
+    pp.L = cp.L;
+    pp.C1 = cp.C1;
+    pp.Lo = cp.Lo;
+    pp.tiles = (cp.Lo + P::TO - 1) / P::TO;
+    pp.x_bytes = cp.x_bytes;
+    pl->pgrid = (int)(a.N * pp.tiles);
+    pl->packed_bytes = a.C <= P::C1MAX ? (int64_t)P::steps((int)a.C) * P::STEP : 0;
     snprintf(pl->text, sizeof(pl->text),
-             "chain bf16 N=%d L=%d C1=%d -> %d -> %d Lo=%d grid=%d (%d outputs per workgroup) lds=%dB%s%s",
-             cp.N, cp.L, cp.C1, S::K, S::K, cp.Lo, pl->grid, S::TO, S::LDS_BYTES, a.has_bias ? " bias" : "",
-             a.gelu ? " gelu" : "");
+             "chain bf16 N=%d L=%d C1=%d -> %d -> %d Lo=%d grid=%d (%d outputs per workgroup) lds=%dB; "
+             "prepacked: grid=%d (%d outputs per workgroup) lds=%dB%s%s",
+             cp.N, cp.L, cp.C1, S::K, S::K, cp.Lo, pl->grid, S::TO, S::LDS_BYTES, pl->pgrid, P::TO, P::LDS_BYTES,
+             a.has_bias ? " bias" : "", a.gelu ? " gelu" : "");
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
     return CONV_OK;
@@ -709,8 +724,86 @@ conv_status_t conv_chain_run(const conv_chain_plan_t *plan, const void *x, const
     return conv_chain_run_events(plan, x, w1, b1, w2, b2, y, stream, nullptr, nullptr);
 }
 
+conv_status_t conv_chain_packed_bytes(const conv_chain_plan_t *plan, int64_t *bytes)
+{
+    if (!plan || !bytes) return fail(CONV_ERR_INVALID_ARG, "plan or bytes is NULL");
+    if (plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "prepacked chain: needs C1 at most %d (C1 = %lld)", ChainPackedShape::C1MAX,
+                    (long long)plan->first.C);
+    *bytes = plan->packed_bytes;
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_pack_weights(const conv_chain_plan_t *plan, const void *w1, const void *w2, void *packed,
+                                      void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "prepacked chain: needs C1 at most %d (C1 = %lld)", ChainPackedShape::C1MAX,
+                    (long long)plan->first.C);
+    if (!w1 || !w2 || !packed) return fail(CONV_ERR_INVALID_ARG, "w1, w2 or packed is NULL");
+    if (((uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)packed) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "w1, w2 and packed must be 16-byte aligned");
+    if (overlaps(packed, plan->packed_bytes, w1, plan->w1_elems * 2) ||
+        overlaps(packed, plan->packed_bytes, w2, plan->w2_elems * 2))
+        return fail(CONV_ERR_INVALID_ARG, "packed overlaps w1 or w2");
+    const int total = (int)(plan->packed_bytes / 16);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(chain_pack_kernel, dim3((total + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                       (const uint4 *)w1, (const uint4 *)w2, (uint4 *)packed, (int)plan->first.C, total);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_run_packed_events(const conv_chain_plan_t *plan, const void *x, const void *packed,
+                                           const void *b1, const void *b2, void *y, void *stream, void *start_event,
+                                           void *stop_event)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    const bool hb = plan->first.has_bias != 0;
+    if (hb && (!b1 || !b2)) return fail(CONV_ERR_INVALID_ARG, "plan has biases but b1 or b2 is NULL");
+    if (!hb && (b1 || b2)) return fail(CONV_ERR_INVALID_ARG, "plan has no bias but b1 or b2 is not NULL");
+    if (plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "prepacked chain: needs C1 at most %d (C1 = %lld)", ChainPackedShape::C1MAX,
+                    (long long)plan->first.C);
+    if (!packed) return fail(CONV_ERR_INVALID_ARG, "packed is NULL");
+    if (plan->y_elems == 0) return CONV_OK;
+    if (!x || !y) return fail(CONV_ERR_INVALID_ARG, "x or y is NULL");
+    if (((uintptr_t)x | (uintptr_t)packed | (uintptr_t)y) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "x, packed and y must be 16-byte aligned");
+    if (((uintptr_t)b1 | (uintptr_t)b2) & 1u) return fail(CONV_ERR_INVALID_ARG, "b1 and b2 must be 2-byte aligned");
+    const int64_t yb = plan->y_elems * 2;
+    if (overlaps(y, yb, x, plan->x_elems * 2) || overlaps(y, yb, packed, plan->packed_bytes) ||
+        overlaps(y, yb, b1, plan->b_elems * 2) || overlaps(y, yb, b2, plan->b_elems * 2))
+        return fail(CONV_ERR_INVALID_ARG, "y overlaps an input");
+    ChainPackedParams pp = plan->pp;
+    pp.x = x; pp.packed = packed; pp.b1 = b1; pp.b2 = b2; pp.y = y;
+    (void)hipGetLastError();
+    const dim3 g(plan->pgrid), blk(256);
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = (hipEvent_t)start_event, e1 = (hipEvent_t)stop_event;
+    if (hb && plan->first.gelu)
+        hipExtLaunchKernelGGL((chain_packed_kernel<true, true>), g, blk, 0, s, e0, e1, 0, pp);
+    else if (hb)
+        hipExtLaunchKernelGGL((chain_packed_kernel<true, false>), g, blk, 0, s, e0, e1, 0, pp);
+    else if (plan->first.gelu)
+        hipExtLaunchKernelGGL((chain_packed_kernel<false, true>), g, blk, 0, s, e0, e1, 0, pp);
+    else
+        hipExtLaunchKernelGGL((chain_packed_kernel<false, false>), g, blk, 0, s, e0, e1, 0, pp);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_run_packed(const conv_chain_plan_t *plan, const void *x, const void *packed, const void *b1,
+                                    const void *b2, void *y, void *stream)
+{
+    return conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream, nullptr, nullptr);
+}
+
 void conv_chain_destroy(conv_chain_plan_t *plan) { delete plan; }
 
 const char *conv_chain_describe(const conv_chain_plan_t *plan) { return plan ? plan->text : ""; }
 
-}  // extern "C\"
+}  // extern "C"

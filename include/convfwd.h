@@ -177,6 +177,34 @@ conv_status_t conv_chain_run_events(const conv_chain_plan_t *plan, const void *x
                                     const void *b1, const void *w2, const void *b2, void *y, void *stream,
                                     void *start_event, void *stop_event);
 
+/* ---- The same chain with prepacked weights -------------------------------
+ * The ExecuTorch conv1d issue's conv2d path (section "The conv2d path
+ * already solves this") prepacks its weights once, ahead of the runs.  Here
+ * the prepacked form puts every 16-element slice of 32 output channels'
+ * weights that one MFMA step consumes in one contiguous kilobyte, so the
+ * kernel streams the weights from L2 with whole-line loads and without
+ * staging them in LDS.  Same results as conv_chain_run for the same inputs
+ * (any summation order within the fp32 bound; bit-identical for
+ * integer-valued inputs).
+ *
+ * conv_chain_packed_bytes: size of the packed weights (a multiple of 16);
+ *   INVALID_ARG for NULL arguments.
+ * conv_chain_pack_weights: enqueues the rearrangement of w1 and w2 (layouts
+ *   as conv_chain_run) into `packed`, a caller-owned device buffer of
+ *   conv_chain_packed_bytes bytes, on `stream`.  All three 16-byte aligned,
+ *   packed not overlapping w1 or w2.  Allocates nothing.  The packed buffer
+ *   stays valid for any run of a plan with the same C1.
+ * conv_chain_run_packed(_events): as conv_chain_run(_events) with the packed
+ *   weights in place of w1 and w2 (16-byte aligned; y must not overlap it). */
+conv_status_t conv_chain_packed_bytes(const conv_chain_plan_t *plan, int64_t *bytes);
+conv_status_t conv_chain_pack_weights(const conv_chain_plan_t *plan, const void *w1, const void *w2, void *packed,
+                                      void *stream);
+conv_status_t conv_chain_run_packed(const conv_chain_plan_t *plan, const void *x, const void *packed,
+                                    const void *b1, const void *b2, void *y, void *stream);
+conv_status_t conv_chain_run_packed_events(const conv_chain_plan_t *plan, const void *x, const void *packed,
+                                           const void *b1, const void *b2, void *y, void *stream,
+                                           void *start_event, void *stop_event);
+
 /* Frees a chain plan (NULL is a no-op). */
 void conv_chain_destroy(conv_chain_plan_t *plan);
 

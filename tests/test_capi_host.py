@@ -305,3 +305,48 @@ def test_chain_run_rejects_bad_arguments_before_launching():
             capi.conv_chain_run(None, 16, 16, 32, 16, 32, 4096)
     finally:
         capi.conv_chain_destroy(plan)
+
+
+@pytest.mark.parametrize("C1,steps", [(80, 16 + 72), (16, 8 + 72), (128, 24 + 72), (224, 48 + 72)])
+def test_chain_packed_bytes(C1, steps):
+    """conv1's 3*C1/16 reduction steps rounded up to whole groups of 8, then
+    conv2's 72; 12 fragments of 1 KB per step."""
+    a, b = _chain_descs(C1=C1)
+    plan = capi.conv_chain_create(a, b)
+    try:
+        assert capi.conv_chain_packed_bytes(plan) == steps * 12 * 1024
+    finally:
+        capi.conv_chain_destroy(plan)
+
+
+def test_chain_packed_rejects_wide_input_and_bad_arguments():
+    a, b = _chain_descs(C1=240)          # the unpacked chain takes it, the prepacked kernel does not
+    plan = capi.conv_chain_create(a, b)
+    try:
+        for call in (lambda: capi.conv_chain_packed_bytes(plan),
+                     lambda: capi.conv_chain_pack_weights(plan, 16, 16, 4096),
+                     lambda: capi.conv_chain_run_packed(plan, 16, 4096, 32, 32, 1 << 20)):
+            with pytest.raises(ConvError) as e:
+                call()
+            assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+    finally:
+        capi.conv_chain_destroy(plan)
+    a, b = _chain_descs()
+    plan = capi.conv_chain_create(a, b)
+    try:
+        nb = capi.conv_chain_packed_bytes(plan)
+        for call in (lambda: capi.conv_chain_pack_weights(plan, None, 16, 1 << 30),          # w1 NULL
+                     lambda: capi.conv_chain_pack_weights(plan, 16, 16, (1 << 30) + 8),     # misaligned
+                     lambda: capi.conv_chain_pack_weights(plan, 16, 1 << 20, (1 << 20) - 64),  # overlaps w2
+                     lambda: capi.conv_chain_run_packed(plan, 16, 4096, None, 32, 1 << 30),   # plan has biases
+                     lambda: capi.conv_chain_run_packed(plan, 16, None, 32, 32, 1 << 30),     # packed NULL
+                     lambda: capi.conv_chain_run_packed(plan, 16, 4104, 32, 32, 1 << 30),     # misaligned
+                     lambda: capi.conv_chain_run_packed(plan, 16, 1 << 30, 32, 32, (1 << 30) + nb - 16),  # overlap
+                     lambda: capi.conv_chain_run_packed(None, 16, 4096, 32, 32, 1 << 30)):
+            with pytest.raises(ConvError) as e:
+                call()
+            assert e.value.status == capi.CONV_ERR_INVALID_ARG, e.value.message
+        with pytest.raises(ConvError):
+            capi.conv_chain_packed_bytes(None)
+    finally:
+        capi.conv_chain_destroy(plan)

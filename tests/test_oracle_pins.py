@@ -464,3 +464,4 @@ def test_chain_bound_accepts_a_float32_chain_and_rejects_a_perturbation():
         bad = g.copy()
         bad[i] = y.ravel()[i] + 3 * st["limit"][i]
         assert not check.check_chain(bad, y, a2, c, p1, p2, True)["ok"]
+

@@ -280,47 +280,81 @@ def _chain(N, L, C1=80):
     return p1, p2
 
 
-def run_chain(dev, p1, p2, x, w1, b1, w2, b2, gelu):
+def run_chain(dev, p1, p2, x, w1, b1, w2, b2, gelu, packed=False):
+    """Runs the fused chain through the C ABI: with the natural weights
+    (conv_chain_run) or prepacked ones (conv_chain_pack_weights, then
+    conv_chain_run_packed)."""
     from convolution_forward_implicit_amd import ConvChain
     c = ConvChain(p1, p2, "bf16", b1 is not None, gelu)
-    print("case: chain", p1, "gelu" if gelu else "", c.describe(), flush=True)
+    print("case: chain", "packed" if packed else "", p1, "gelu" if gelu else "", c.describe(), flush=True)
     t = lambda a: None if a is None else to_dev(a, "bf16", dev)
-    y = c(t(x), t(w1), t(b1), t(w2), t(b2))
+    if packed:
+        y = c.run_packed(t(x), c.pack(t(w1), t(w2)), t(b1), t(b2))
+    else:
+        y = c(t(x), t(w1), t(b1), t(w2), t(b2))
     torch.cuda.synchronize()
     return y, c
 
 
-@pytest.mark.parametrize("N,L,C1", [(2, 300, 80), (3, 1001, 80), (1, 130, 16), (2, 257, 352)])
-def test_chain_integer_bit_exact(dev, N, L, C1):
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("N,L,C1", [(2, 300, 80), (3, 1001, 80), (1, 130, 16), (2, 257, 352), (2, 190, 224),
+                                    (1, 2, 128), (1, 1, 80)])
+def test_chain_integer_bit_exact(dev, N, L, C1, packed):
     """Integer inputs: conv1's fp32 sums are exact, so the device's bf16 h is
     the oracle's rounding of the exact h, conv2's sums of those bf16 values
     are exact too, and the bf16 output has one correct value."""
+    if packed and C1 > 224:
+        pytest.skip("the prepacked kernel takes C1 <= 224 (conv_chain_packed_bytes says UNSUPPORTED)")
     p1, p2 = _chain(N, L, C1)
     x, w1, b1 = sd.random_inputs(p1, "bf16", 81, True, kind="int")
     _, w2, b2 = sd.random_inputs(p2, "bf16", 82, True, kind="int")
-    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, False)
+    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, False, packed)
     r, _, _ = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, False)
     assert np.array_equal(bits(y).ravel(), check.round_to_bf16_bits(r).ravel())
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("N,L", [(2, 301), (1, 64), (2, 127)])
-def test_chain_seeded_float_parity(dev, N, L):
+def test_chain_seeded_float_parity(dev, N, L, packed):
     p1, p2 = _chain(N, L)
     x, w1, b1 = sd.random_inputs(p1, "bf16", 83, True)
     _, w2, b2 = sd.random_inputs(p2, "bf16", 84, True)
-    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, True)
+    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, True, packed)
     r, a2, cy = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, True)
     st = check.check_chain(host(y), r, a2, cy, p1, p2, True)
     print("parity:", {k: v for k, v in st.items() if k != "limit"}, flush=True)
     assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
 
 
-def test_chain_workload_full_size_sampled(dev):
+def test_chain_packed_no_bias_no_gelu_and_pack_layout(dev):
+    """Without bias and GELU; and the packed weights are a rearrangement of
+    w1 and w2 with zero padding: every nonzero 16-byte chunk of w1 and w2
+    appears, and the packed byte count is what conv_chain_packed_bytes says."""
+    p1, p2 = _chain(2, 211, 48)
+    x, w1, _ = sd.random_inputs(p1, "bf16", 86, False)
+    _, w2, _ = sd.random_inputs(p2, "bf16", 87, False)
+    y, c = run_chain(dev, p1, p2, x, w1, None, w2, None, False, True)
+    r, a2, cy = ref.conv_chain(p1, p2, x, w1, None, w2, None, False)
+    st = check.check_chain(host(y), r, a2, cy, p1, p2, False)
+    assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
+    pk = c.pack(to_dev(w1, "bf16", dev), to_dev(w2, "bf16", dev))
+    torch.cuda.synchronize()
+    assert pk.numel() == c.packed_bytes()
+    chunks = pk.cpu().numpy().view(np.uint16).reshape(-1, 8)
+    nat = np.concatenate([bits(to_dev(w1, "bf16", dev)).reshape(-1, 8), bits(to_dev(w2, "bf16", dev)).reshape(-1, 8)])
+    assert chunks.shape[0] == c.packed_bytes() // 16
+    key = lambda a: np.ascontiguousarray(a).view(np.dtype((np.void, 16))).ravel()
+    nonzero = chunks[(chunks != 0).any(axis=1)]
+    assert np.array_equal(np.sort(key(nonzero)), np.sort(key(nat[(nat != 0).any(axis=1)])))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_chain_workload_full_size_sampled(dev, packed):
     """The batch-32 bf16 frontend at full size, in the launch the benchmark
     times with --fused: 4000 random outputs plus borders against the oracle."""
     W = sd.workload(3)
     (p1, _, _), (p2, _, _) = W["layers"]
-    y, _ = run_chain(dev, p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True)
+    y, _ = run_chain(dev, p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True, packed)
     idx = sample_indices(p2, 4000, 85)
     r, a2, cy = ref.conv_chain_points(p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True, idx)
     st = check.check_chain(host(y).ravel()[idx], r, a2, cy, p1, p2, True)
