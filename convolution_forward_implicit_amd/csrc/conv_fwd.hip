@@ -56,7 +56,7 @@ void launch_reg(const KParams &kp, uint32_t, uint32_t, int grid, hipStream_t s, 
 
 // The epilogue (bias, GELU) is compiled into each kernel variant, so a
 // variant carries only the code it runs.
-template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB>
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG>
 void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
                 hipEvent_t e1)
 {
@@ -64,16 +64,16 @@ void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream
     dp.k = kp;
     dp.x_bytes = xb;
     dp.w_bytes = wb;
-    const dim3 g(grid), b(WM * WN * 64);
+    const dim3 g(grid), b(WM * WN * 64 * KG);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, true>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, true, true>), g, b, 0, s, e0, e1, 0, dp);
     else if (bias)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, true, false>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, true, false>), g, b, 0, s, e0, e1, 0, dp);
     else if (kp.gelu)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, true>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, false, true>), g, b, 0, s, e0, e1, 0, dp);
     else
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, false, false>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, false, false>), g, b, 0, s, e0, e1, 0, dp);
 }
 
 FastDiv make_fastdiv(int d);
@@ -115,6 +115,7 @@ struct TileCfg {
     launch_fn fn;
     const char *name;
     int TH, TW, CC, PHMAX, PWMAX, TAPMAX;   // KIND_PATCH only
+    int KG;             // KIND_DMA: reduction groups per workgroup (0 means 1)
 };
 
 #define CFG(DT, BM, BN, BK, WM, WN, VEC)                                                 \
@@ -127,11 +128,20 @@ struct TileCfg {
 
 #define DMA(DT, BM, BN, WM, WN, NS, MF, KSUB)                                            \
     TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
-            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB>::LDS_BYTES,                        \
-            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB>,                               \
+            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, 1>::LDS_BYTES,                     \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1>,                            \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB  \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB), \
-            0, 0, 0, 0, 0, 0}
+            0, 0, 0, 0, 0, 0, 1}
+
+// Two reduction groups per workgroup (twice the waves, half the K-steps each)
+#define DMA2(DT, BM, BN, WM, WN, NS, MF, KSUB)                                           \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
+            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, 2>::LDS_BYTES,                     \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 2>,                            \
+            (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2" \
+                : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2"), \
+            0, 0, 0, 0, 0, 0, 2}
 
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
@@ -183,6 +193,15 @@ const TileCfg kCfgs[] = {
     DMA(0, 64, 32, 4, 1, 2, 16, 2),
     DMA(0, 64, 64, 2, 2, 2, 16, 1),
     DMA(0, 64, 64, 2, 2, 2, 16, 2),
+    DMA2(0, 32, 32, 2, 2, 2, 16, 2),
+    DMA2(0, 32, 32, 2, 2, 2, 16, 1),
+    DMA2(0, 32, 64, 1, 4, 2, 16, 2),
+    DMA2(0, 32, 64, 1, 4, 2, 16, 1),
+    DMA2(0, 64, 32, 4, 1, 2, 16, 1),
+    DMA2(0, 64, 64, 2, 2, 2, 16, 1),
+    DMA2(1, 128, 64, 2, 2, 2, 32, 1),
+    DMA2(1, 64, 64, 2, 2, 2, 16, 1),
+    DMA2(1, 128, 32, 4, 1, 2, 16, 1),
     CFG(1, 128, 128, 64, 2, 2, 8),
     CFG(1, 128, 64, 64, 2, 2, 8),
     CFG(1, 128, 32, 64, 4, 1, 8),
@@ -394,7 +413,8 @@ double steps_of(const TileCfg &c, const conv_fwd_desc_t &d)
 {
     if (c.kind == KIND_PATCH) return (double)d.filt[0] * (double)(d.C / c.CC);
     const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
-    return (double)((Kred + c.BK - 1) / c.BK);
+    const int64_t kg = c.KG > 1 ? c.KG : 1;
+    return (double)(((Kred + c.BK - 1) / c.BK + kg - 1) / kg);   // K-steps of one reduction group
 }
 
 // Predicted milliseconds of one configuration on the plan's problem.

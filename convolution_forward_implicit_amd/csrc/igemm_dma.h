@@ -82,15 +82,15 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB>
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG = 1>
 struct DmaShape {
     using T = typename Elem<DT>::type;
     static constexpr int ESZ = (int)sizeof(T);
     static constexpr int VEC = 16 / ESZ;          // elements per 16-byte chunk
     static constexpr int SUBK = 128 / ESZ;        // reduction elements per 128-byte sub-slice
     static constexpr int BK = SUBK * KSUB;        // reduction elements per K-step
-    static constexpr int NW = WM * WN;
-    static constexpr int NT = NW * 64;
+    static constexpr int NW = WM * WN;            // waves of one reduction group
+    static constexpr int NT = NW * 64 * KG;       // threads of the workgroup
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int MI = TM / MF, NI = TN / MF;   // MFMA blocks per wave
     static constexpr int ACC = MF * MF / 64;          // accumulator floats per lane and block
@@ -101,20 +101,23 @@ struct DmaShape {
     static constexpr int STAGE = SUB * KSUB;
     static constexpr int LDC = BN + VEC;
     static constexpr int EPI = BM * LDC * ESZ;
-    static constexpr int LDS_BYTES = NS * STAGE > EPI ? NS * STAGE : EPI;
+    static constexpr int PART = (KG - 1) * BM * BN * 4;   // other group's fp32 partial tile
+    static constexpr int PIPE = KG * NS * STAGE;
+    static constexpr int LDS_BYTES = PIPE > EPI ? (PIPE > PART ? PIPE : PART) : (EPI > PART ? EPI : PART);
 
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole DMA blocks per wave");
     static_assert(TM % MF == 0 && TN % MF == 0, "whole MFMA blocks per wave");
     static_assert(MF == 16 || (MF == 32 && DT == 1), "32x32 blocks: bf16 only");
     static_assert(NS >= 2 && L * (NS - 2) < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
+    static_assert(KG == 1 || KG == 2, "one or two reduction groups");
 };
 
-template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, bool BIAS, bool GELU>
-__global__ void __launch_bounds__(WM * WN * 64)
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG, bool BIAS, bool GELU>
+__global__ void __launch_bounds__(WM * WN * 64 * KG)
 igemm_dma_kernel(DmaParams dp)
 {
-    using S = DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB>;
+    using S = DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, KG>;
     using AccT = typename std::conditional<MF == 32, f32x16_t, f32x4_t>::type;
     using T = typename S::T;
     const KParams &p = dp.k;
@@ -124,7 +127,17 @@ igemm_dma_kernel(DmaParams dp)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // With KG = 2 the workgroup is two groups of WM x WN waves that split the
+    // reduction: group kg runs K-steps kg*nkh .. kg*nkh + nkh - 1 (steps past
+    // the end load zeros) through its own LDS stages, and group 1 hands its
+    // partial tile to group 0 through LDS at the end, which adds it (a fixed
+    // order, so the sum is deterministic).  Twice the waves per tile, half the
+    // serial K-steps each: it pays for problems with few output tiles and a
+    // long reduction (measured 10-15% on 7x7 and 14x14 maps with 256-512
+    // channels; no change on the frontend layers).
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave_all / S::NW;
+    const int wave = wave_all - kg * S::NW;   // wave within the group
     const int wm = wave / WN;
     const int wn = wave % WN;
 
@@ -197,9 +210,14 @@ igemm_dma_kernel(DmaParams dp)
         b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + cht * S::VEC) * S::ESZ) : kOutOfRange;
     }
 
+    // K-steps of this group: kstart .. kstart + nkh - 1
+    const int nk = (p.Kred + S::BK - 1) / S::BK;
+    const int nkh = (nk + KG - 1) / KG;
+    const int kstart = kg * nkh;
+
     // filter tap of reduction index r = k0 + chunk*VEC, stepped by one
-    // 128-byte sub-slice (SUBK elements) per call of issue_sub
-    int r = chunk * S::VEC;
+    // 128-byte sub-slice (SUBK elements) per call of prep
+    int r = kstart * S::BK + chunk * S::VEC;
     int c, xk, yk, zk;
     {
         const int tap = fdiv(r, p.fd_C);
@@ -248,7 +266,7 @@ igemm_dma_kernel(DmaParams dp)
     // load number q (0 .. L-1) of the prepared stage into LDS stage `stage`
     auto fire = [&](int stage, int q) {
         const int u = q / LPS, t = q % LPS;
-        const uint32_t base = lds0 + stage * S::STAGE + u * S::SUB;
+        const uint32_t base = lds0 + (kg * NS + stage) * S::STAGE + u * S::SUB;
         if (t < S::A_PER_W)
             dma16(xr, dv[u][t], 0, base + (wave * S::A_PER_W + t) * 1024);
         else
@@ -281,7 +299,7 @@ igemm_dma_kernel(DmaParams dp)
     auto compute = [&](int stage, int dst) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
-            const unsigned char *As = smem + stage * S::STAGE + u * S::SUB;
+            const unsigned char *As = smem + (kg * NS + stage) * S::STAGE + u * S::SUB;
             const unsigned char *Bs = As + BM * 128;
             typedef typename std::conditional<DT == 1, bf16x8_t, f32x4_t>::type Frag;
             Frag a[QS][S::MI], b[QS][S::NI];
@@ -327,20 +345,20 @@ igemm_dma_kernel(DmaParams dp)
     };
 
     // ---- pipeline: stage it+NS-1 is loaded while stage it is multiplied ---
-    const int nk = (p.Kred + S::BK - 1) / S::BK;
+    // (both groups run the same nkh steps, so every barrier sees all waves)
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
-        if (s < nk) {
-            prep(s * S::BK);
+        if (s < nkh) {
+            prep((kstart + s) * S::BK);
 #pragma unroll
             for (int q = 0; q < S::L; ++q) fire(s, q);
         }
-    for (int it = 0; it < nk - 1; ++it) {
-        if (it + NS - 2 < nk) wait_vmcnt<S::L * (NS - 2)>();
+    for (int it = 0; it < nkh - 1; ++it) {
+        if (it + NS - 2 < nkh) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();                        // step it is in LDS for every wave
-        const bool more = it + NS - 1 < nk;     // the buffer it refills was read in step it-1
-        if (more) prep((it + NS - 1) * S::BK);
+        const bool more = it + NS - 1 < nkh;    // the buffer it refills was read in step it-1
+        if (more) prep((kstart + it + NS - 1) * S::BK);
         compute(it % NS, more ? (it + NS - 1) % NS : -1);
     }
     // last step: nothing left to load
@@ -362,14 +380,40 @@ igemm_dma_kernel(DmaParams dp)
                     bias_v[j][h][e] = n < p.K ? v : 0.f;
                 }
     }
-    compute((nk - 1) % NS, -1);
+    compute((nkh - 1) % NS, -1);
     __syncthreads();
+
+    // ---- group 1's partial tile into group 0's accumulators ---------------
+    if constexpr (KG == 2) {
+        float *part = reinterpret_cast<float *>(smem);   // [wave][i][j][e][lane]
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+                    for (int e = 0; e < S::ACC; ++e)
+                        part[(((wave * S::MI + i) * S::NI + j) * S::ACC + e) * 64 + lane] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+#pragma unroll
+                    for (int e = 0; e < S::ACC; ++e)
+                        acc[i][j][e] += part[(((wave * S::MI + i) * S::NI + j) * S::ACC + e) * 64 + lane];
+        }
+        __syncthreads();                        // the staging below reuses the same bytes
+    }
 
     // ---- epilogue: bias, GELU, round, stage in LDS, whole-vector stores ---
     // Transposed product: in a 16x16 block the lane holds channels
     // 4*fk + e (e = 0..3) of pixel frow; in a 32x32 block it holds channels
     // 8*h + 4*fk + e (h = 0..3, e = 0..3) of pixel frow.
     T *Cs = reinterpret_cast<T *>(smem);
+    if (kg == 0) {
 #pragma unroll
     for (int j = 0; j < S::NI; ++j)
 #pragma unroll
@@ -399,6 +443,7 @@ igemm_dma_kernel(DmaParams dp)
                 }
             }
         }
+    }
     __syncthreads();
 
     T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;

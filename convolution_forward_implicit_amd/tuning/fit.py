@@ -30,17 +30,18 @@ CUS = 256
 
 
 def cfg_tile(name):
-    """(BM, BN, BK) of an implicit-GEMM configuration, or ("patch", TH, TW,
-    BN, CC) of an input-patch one."""
+    """(BM, BN, BK, KG) of an implicit-GEMM configuration (KG reduction
+    groups per workgroup), or ("patch", TH, TW, BN, CC) of an input-patch
+    one."""
     m = re.match(r"bf16_patch_(\d+)x(\d+)x(\d+)_c(\d+)_s\d_p\d+x\d+_d\d$", name)
     if m:
         return ("patch",) + tuple(int(v) for v in m.groups())
-    m = re.match(r"(f32|bf16)_dma_(\d+)x(\d+)_w\dx\d_s\d_m\d+_k(\d)$", name)
+    m = re.match(r"(f32|bf16)_dma_(\d+)x(\d+)_w\dx\d_s\d_m\d+_k(\d)(_g2)?$", name)
     if m:
         esz = 2 if m.group(1) == "bf16" else 4
-        return int(m.group(2)), int(m.group(3)), int(m.group(4)) * 128 // esz
+        return int(m.group(2)), int(m.group(3)), int(m.group(4)) * 128 // esz, 2 if m.group(5) else 1
     m = re.match(r"(f32|bf16)_(\d+)x(\d+)x(\d+)_w\dx\d_v\d$", name)
-    return int(m.group(2)), int(m.group(3)), int(m.group(4))
+    return int(m.group(2)), int(m.group(3)), int(m.group(4)), 1
 
 
 def features(prob, name):
@@ -54,10 +55,10 @@ def features(prob, name):
         tiles = prob["N"] * o[0] * math.ceil(o[1] / TH) * math.ceil(o[2] / TW) * math.ceil(prob["K"] / BN) * prob["G"]
         nk = prob["filt"][0] * (prob["C"] // CC)
     else:
-        BM, BN, BK = t
+        BM, BN, BK, KG = t
         M = prob["N"] * o[0] * o[1] * o[2]
         tiles = math.ceil(M / BM) * math.ceil(prob["K"] / BN) * prob["G"]
-        nk = math.ceil(prob["C"] * prob["filt"][0] * prob["filt"][1] * prob["filt"][2] / BK)
+        nk = math.ceil(math.ceil(prob["C"] * prob["filt"][0] * prob["filt"][1] * prob["filt"][2] / BK) / KG)
     r = math.ceil(tiles / CUS)
     g = 1.0 if prob.get("gelu") else 0.0
     return [1.0, float(r), float(r * nk), float(nk), g * r]
