@@ -1,6 +1,7 @@
 /*
- * Forward-convolution oracle: plain direct nested-loop cross-correlation in
- * double precision.  TEST INFRASTRUCTURE ONLY -- the library never links,
+ * Convolution oracle: plain direct nested-loop cross-correlation in double
+ * precision, and its two backward passes (input and weight gradients,
+ * below the forward code).  TEST INFRASTRUCTURE ONLY -- the library never links,
  * loads or calls this file; only the tests, the smoke check and the
  * benchmark's CPU-baseline leg do.
  *
@@ -163,6 +164,191 @@ int oracle_conv_fwd_points(const oracle_desc *d, const double *x, const double *
         double yv, ad;
         one_output(d, o, x, w, b, gelu, n, od, oh, ow, g, k, &yv, &ad);
         y[i] = yv;
+        if (absdot) absdot[i] = ad;
+    }
+    return 0;
+}
+
+/* ---- Backward passes -----------------------------------------------------
+ * The Composable Kernel note (section 6, "Backward Variants Not Yet
+ * Upgraded") names the bf16 grouped backward-data and backward-weight
+ * convolutions on gfx950 beside the forward one, in the same layouts.  Their
+ * plain definitions are the two partial derivatives of the forward sum
+ * above (no bias, no activation: the backward of the linear convolution):
+ *
+ *   dx[n,id,ih,iw,g,c] = sum over (z,y,x,k) and the output (od,oh,ow) with
+ *        od*sd - pd + z*dd = id, oh*sh - ph + y*dh = ih, ow*sw - pw + x*dw = iw
+ *        of  dy[n,od,oh,ow,g,k] * w[g,k,z,y,x,c]
+ *   dw[g,k,z,y,x,c] = sum over (n,od,oh,ow) whose tap (z,y,x) lies inside
+ *        the input of  dy[n,od,oh,ow,g,k] * x[n,id,ih,iw,g,c]
+ *
+ * dx has x's layout, dw has w's; absdot holds the matching sums of |terms|.
+ */
+
+/* Output coordinate that tap t of an output reads input coordinate i with,
+ * or -1 when no output does (o*s - p + t*d = i has no solution in range). */
+static int64_t out_of(int64_t i, int64_t t, int64_t s, int64_t p, int64_t d, int64_t O)
+{
+    int64_t num = i + p - t * d;
+    if (num < 0 || num % s != 0) return -1;
+    num /= s;
+    return num < O ? num : -1;
+}
+
+static void one_dx(const oracle_desc *d, const int64_t o[3], const double *dy, const double *w,
+                   int64_t n, int64_t id, int64_t ih, int64_t iw, int64_t g, int64_t c,
+                   double *v, double *ad)
+{
+    const int64_t Z = d->filt[0], Y = d->filt[1], X = d->filt[2];
+    const int64_t G = d->G, C = d->C, K = d->K;
+    double acc = 0.0, absacc = 0.0;
+    for (int64_t z = 0; z < Z; ++z) {
+        int64_t od = out_of(id, z, d->stride[0], d->pad[0], d->dil[0], o[0]);
+        if (od < 0) continue;
+        for (int64_t y = 0; y < Y; ++y) {
+            int64_t oh = out_of(ih, y, d->stride[1], d->pad[1], d->dil[1], o[1]);
+            if (oh < 0) continue;
+            for (int64_t xx = 0; xx < X; ++xx) {
+                int64_t ow = out_of(iw, xx, d->stride[2], d->pad[2], d->dil[2], o[2]);
+                if (ow < 0) continue;
+                const double *dyp = dy + ((((n * o[0] + od) * o[1] + oh) * o[2] + ow) * G + g) * K;
+                for (int64_t k = 0; k < K; ++k) {
+                    double p = dyp[k] * w[((((g * K + k) * Z + z) * Y + y) * X + xx) * C + c];
+                    acc += p;
+                    absacc += fabs(p);
+                }
+            }
+        }
+    }
+    *v = acc;
+    *ad = absacc;
+}
+
+/* Full input gradient: dx (and absdot, when not NULL) hold N*Di*Hi*Wi*G*C
+ * doubles.  Returns 0, or -1 on a degenerate descriptor. */
+int oracle_conv_bwd_data(const oracle_desc *d, const double *dy, const double *w, double *dx, double *absdot)
+{
+    int64_t o[3];
+    if (oracle_out_dims(d, o) != 0) return -1;
+    const int64_t Di = d->in[0], Hi = d->in[1], Wi = d->in[2], G = d->G, C = d->C;
+    const int64_t rows = d->N * Di * Hi;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t n = r / (Di * Hi), id = (r / Hi) % Di, ih = r % Hi;
+        for (int64_t iw = 0; iw < Wi; ++iw)
+            for (int64_t g = 0; g < G; ++g)
+                for (int64_t c = 0; c < C; ++c) {
+                    int64_t idx = ((((n * Di + id) * Hi + ih) * Wi + iw) * G + g) * C + c;
+                    double v, ad;
+                    one_dx(d, o, dy, w, n, id, ih, iw, g, c, &v, &ad);
+                    dx[idx] = v;
+                    if (absdot) absdot[idx] = ad;
+                }
+    }
+    return 0;
+}
+
+/* Selected input-gradient elements (flat indices into the x layout).
+ * Returns 0, -1 on a degenerate descriptor, -2 on an index out of range. */
+int oracle_conv_bwd_data_points(const oracle_desc *d, const double *dy, const double *w, int64_t npts,
+                                const int64_t *idx, double *dx, double *absdot)
+{
+    int64_t o[3];
+    if (oracle_out_dims(d, o) != 0) return -1;
+    const int64_t Di = d->in[0], Hi = d->in[1], Wi = d->in[2], G = d->G, C = d->C;
+    const int64_t total = d->N * Di * Hi * Wi * G * C;
+    for (int64_t i = 0; i < npts; ++i)
+        if (idx[i] < 0 || idx[i] >= total) return -2;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < npts; ++i) {
+        int64_t t = idx[i];
+        int64_t c = t % C;  t /= C;
+        int64_t g = t % G;  t /= G;
+        int64_t iw = t % Wi; t /= Wi;
+        int64_t ih = t % Hi; t /= Hi;
+        int64_t id = t % Di; t /= Di;
+        double v, ad;
+        one_dx(d, o, dy, w, t, id, ih, iw, g, c, &v, &ad);
+        dx[i] = v;
+        if (absdot) absdot[i] = ad;
+    }
+    return 0;
+}
+
+static void one_dw(const oracle_desc *d, const int64_t o[3], const double *x, const double *dy,
+                   int64_t g, int64_t k, int64_t z, int64_t y, int64_t xx, int64_t c, double *v, double *ad)
+{
+    const int64_t Di = d->in[0], Hi = d->in[1], Wi = d->in[2];
+    const int64_t G = d->G, C = d->C, K = d->K;
+    double acc = 0.0, absacc = 0.0;
+    for (int64_t n = 0; n < d->N; ++n)
+        for (int64_t od = 0; od < o[0]; ++od) {
+            int64_t id = od * d->stride[0] - d->pad[0] + z * d->dil[0];
+            if (id < 0 || id >= Di) continue;
+            for (int64_t oh = 0; oh < o[1]; ++oh) {
+                int64_t ih = oh * d->stride[1] - d->pad[1] + y * d->dil[1];
+                if (ih < 0 || ih >= Hi) continue;
+                for (int64_t ow = 0; ow < o[2]; ++ow) {
+                    int64_t iw = ow * d->stride[2] - d->pad[2] + xx * d->dil[2];
+                    if (iw < 0 || iw >= Wi) continue;
+                    double p = dy[((((n * o[0] + od) * o[1] + oh) * o[2] + ow) * G + g) * K + k] *
+                               x[((((n * Di + id) * Hi + ih) * Wi + iw) * G + g) * C + c];
+                    acc += p;
+                    absacc += fabs(p);
+                }
+            }
+        }
+    *v = acc;
+    *ad = absacc;
+}
+
+/* Full weight gradient: dw (and absdot, when not NULL) hold G*K*Z*Y*X*C
+ * doubles.  Returns 0, or -1 on a degenerate descriptor. */
+int oracle_conv_bwd_weight(const oracle_desc *d, const double *x, const double *dy, double *dw, double *absdot)
+{
+    int64_t o[3];
+    if (oracle_out_dims(d, o) != 0) return -1;
+    const int64_t Z = d->filt[0], Y = d->filt[1], X = d->filt[2], C = d->C;
+    const int64_t rows = d->G * d->K;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t g = r / d->K, k = r % d->K;
+        for (int64_t z = 0; z < Z; ++z)
+            for (int64_t y = 0; y < Y; ++y)
+                for (int64_t xx = 0; xx < X; ++xx)
+                    for (int64_t c = 0; c < C; ++c) {
+                        int64_t idx = (((r * Z + z) * Y + y) * X + xx) * C + c;
+                        double v, ad;
+                        one_dw(d, o, x, dy, g, k, z, y, xx, c, &v, &ad);
+                        dw[idx] = v;
+                        if (absdot) absdot[idx] = ad;
+                    }
+    }
+    return 0;
+}
+
+/* Selected weight-gradient elements (flat indices into the w layout).
+ * Returns 0, -1 on a degenerate descriptor, -2 on an index out of range. */
+int oracle_conv_bwd_weight_points(const oracle_desc *d, const double *x, const double *dy, int64_t npts,
+                                  const int64_t *idx, double *dw, double *absdot)
+{
+    int64_t o[3];
+    if (oracle_out_dims(d, o) != 0) return -1;
+    const int64_t Z = d->filt[0], Y = d->filt[1], X = d->filt[2], C = d->C, K = d->K;
+    const int64_t total = d->G * K * Z * Y * X * C;
+    for (int64_t i = 0; i < npts; ++i)
+        if (idx[i] < 0 || idx[i] >= total) return -2;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < npts; ++i) {
+        int64_t t = idx[i];
+        int64_t c = t % C;  t /= C;
+        int64_t xx = t % X; t /= X;
+        int64_t y = t % Y;  t /= Y;
+        int64_t z = t % Z;  t /= Z;
+        int64_t k = t % K;  t /= K;
+        double v, ad;
+        one_dw(d, o, x, dy, t, k, z, y, xx, c, &v, &ad);
+        dw[i] = v;
         if (absdot) absdot[i] = ad;
     }
     return 0;

@@ -19,7 +19,11 @@ conv1d == conv2d(H=1) == conv3d(D=H=1); grouped == G independent convs;
 delta kernel; all-ones border counts; 1x1 conv == matmul; single-channel
 conv == numpy.correlate; linearity; GELU closed forms; bf16 rounding against
 IEEE bit patterns and hand-worked ties; the two-conv chain against delta
-filters (closed form) and against the composed 5-tap kernel (interior).
+filters (closed form) and against the composed 5-tap kernel (interior); the
+backward passes as the adjoints of the forward sum (<conv(x,w), dy> =
+<x, dgrad> = <w, wgrad> on the exhaustive tiny grid, plus one-hot forward
+probes), against torch's fp64 autograd, a delta kernel's scatter and the
+all-ones valid-output counts.
 """
 import ctypes
 import math
@@ -59,6 +63,12 @@ def _load():
         lib.oracle_conv_fwd_points.argtypes = [ctypes.POINTER(_Desc), dp, dp, dp,
                                                ctypes.c_int, ctypes.c_int64, ip, dp, dp]
         lib.oracle_conv_fwd_points.restype = ctypes.c_int
+        for name in ("oracle_conv_bwd_data", "oracle_conv_bwd_weight"):
+            getattr(lib, name).argtypes = [ctypes.POINTER(_Desc), dp, dp, dp, dp]
+            getattr(lib, name).restype = ctypes.c_int
+        for name in ("oracle_conv_bwd_data_points", "oracle_conv_bwd_weight_points"):
+            getattr(lib, name).argtypes = [ctypes.POINTER(_Desc), dp, dp, ctypes.c_int64, ip, dp, dp]
+            getattr(lib, name).restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -142,6 +152,68 @@ def conv_fwd_points(p, x, w, b, gelu, flat_idx):
     if rc != 0:
         raise ValueError("oracle_conv_fwd_points failed (%d)" % rc)
     return y, ad
+
+
+def conv_bwd_data(p, dy, w):
+    """Gradient with respect to the input (x's layout, float64) of the
+    forward sum for output gradient dy, and the per-element sum of |terms|:
+    (dx, absdot).  No bias or activation (the backward of the linear conv)."""
+    xs, ws, _, ys = shapes(p)
+    dy = _as_f64(dy, ys, "dy")
+    w = _as_f64(w, ws, "w")
+    dx = np.empty(xs, dtype=np.float64)
+    ad = np.empty(xs, dtype=np.float64)
+    rc = _load().oracle_conv_bwd_data(ctypes.byref(_mk_desc(p)), _dptr(dy), _dptr(w), _dptr(dx), _dptr(ad))
+    if rc != 0:
+        raise ValueError("oracle_conv_bwd_data failed (%d)" % rc)
+    return dx, ad
+
+
+def conv_bwd_data_points(p, dy, w, flat_idx):
+    """conv_bwd_data at flat indices of the x layout: (values, absdot)."""
+    xs, ws, _, ys = shapes(p)
+    dy = _as_f64(dy, ys, "dy")
+    w = _as_f64(w, ws, "w")
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    v = np.empty(idx.shape, dtype=np.float64)
+    ad = np.empty(idx.shape, dtype=np.float64)
+    rc = _load().oracle_conv_bwd_data_points(ctypes.byref(_mk_desc(p)), _dptr(dy), _dptr(w), idx.size,
+                                             idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(v),
+                                             _dptr(ad))
+    if rc != 0:
+        raise ValueError("oracle_conv_bwd_data_points failed (%d)" % rc)
+    return v, ad
+
+
+def conv_bwd_weight(p, x, dy):
+    """Gradient with respect to the weights (w's layout, float64) for input
+    x and output gradient dy, and the per-element sum of |terms|: (dw,
+    absdot)."""
+    xs, ws, _, ys = shapes(p)
+    x = _as_f64(x, xs, "x")
+    dy = _as_f64(dy, ys, "dy")
+    dw = np.empty(ws, dtype=np.float64)
+    ad = np.empty(ws, dtype=np.float64)
+    rc = _load().oracle_conv_bwd_weight(ctypes.byref(_mk_desc(p)), _dptr(x), _dptr(dy), _dptr(dw), _dptr(ad))
+    if rc != 0:
+        raise ValueError("oracle_conv_bwd_weight failed (%d)" % rc)
+    return dw, ad
+
+
+def conv_bwd_weight_points(p, x, dy, flat_idx):
+    """conv_bwd_weight at flat indices of the w layout: (values, absdot)."""
+    xs, ws, _, ys = shapes(p)
+    x = _as_f64(x, xs, "x")
+    dy = _as_f64(dy, ys, "dy")
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    v = np.empty(idx.shape, dtype=np.float64)
+    ad = np.empty(idx.shape, dtype=np.float64)
+    rc = _load().oracle_conv_bwd_weight_points(ctypes.byref(_mk_desc(p)), _dptr(x), _dptr(dy), idx.size,
+                                               idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(v),
+                                               _dptr(ad))
+    if rc != 0:
+        raise ValueError("oracle_conv_bwd_weight_points failed (%d)" % rc)
+    return v, ad
 
 
 def round_bf16(v):

@@ -465,3 +465,115 @@ def test_chain_bound_accepts_a_float32_chain_and_rejects_a_perturbation():
         bad[i] = y.ravel()[i] + 3 * st["limit"][i]
         assert not check.check_chain(bad, y, a2, c, p1, p2, True)["ok"]
 
+
+
+# --------------------------------------------------------------------------
+# Backward passes (oracle.ref.conv_bwd_data / conv_bwd_weight), pinned to the
+# pinned forward sum and to torch's autograd in fp64.
+@pytest.mark.parametrize("idx", range(len(GRID)))
+def test_backward_passes_are_the_adjoints_of_the_forward_sum(idx):
+    """<conv(x, w), dy> = <x, dgrad(dy, w)> = <w, wgrad(x, dy)> for random
+    x, w, dy: the two gradients of the bilinear forward map.  Any index, sign
+    or stride mistake in either backward loop breaks one of the equalities
+    (the forward sum itself is pinned above)."""
+    p = GRID[idx]
+    xs, ws, _, ys = ref.shapes(p)
+    rng = np.random.default_rng(500 + idx)
+    x, w, dy = rng.standard_normal(xs), rng.standard_normal(ws), rng.standard_normal(ys)
+    y = ref.conv_fwd(p, x, w, None, False, want_absdot=False)
+    dx, adx = ref.conv_bwd_data(p, dy, w)
+    dw, adw = ref.conv_bwd_weight(p, x, dy)
+    lhs = float(np.sum(y * dy))
+    scale = float(np.sum(np.abs(y) * np.abs(dy))) + 1.0
+    assert abs(lhs - float(np.sum(x * dx))) <= 1e-12 * scale
+    assert abs(lhs - float(np.sum(w * dw))) <= 1e-12 * scale
+    # and each one against its own brute force: dx[i] = d<y, dy>/dx[i] as the
+    # forward of a one-hot x, dw likewise, at a few random elements
+    for _ in range(3):
+        i = tuple(int(rng.integers(0, s)) for s in xs)
+        e = np.zeros(xs); e[i] = 1.0
+        assert abs(np.sum(ref.conv_fwd(p, e, w, None, False, want_absdot=False) * dy) - dx[i]) <= 1e-12 * (1 + adx[i])
+        j = tuple(int(rng.integers(0, s)) for s in ws)
+        e = np.zeros(ws); e[j] = 1.0
+        assert abs(np.sum(ref.conv_fwd(p, x, e, None, False, want_absdot=False) * dy) - dw[j]) <= 1e-12 * (1 + adw[j])
+
+
+@pytest.mark.parametrize("p", [
+    sd.conv1d_problem(2, 384, 64, 301, 3, 2, 1),
+    sd.problem(2, 4, 16, 8, (1, 13, 11), (1, 3, 3), (1, 2, 1), (0, 1, 2), (1, 1, 2)),
+    sd.problem(1, 8, 8, 4, (6, 9, 9), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2)),
+    sd.problem(1, 2, 5, 3, (4, 5, 7), (2, 1, 3), (2, 1, 3), (1, 0, 1), (1, 1, 1)),
+], ids=["conv1d_s2", "grouped2d", "grouped3d_dil2", "odd3d"])
+def test_backward_passes_match_torch_autograd_fp64(p):
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    N, G, C, K = p["N"], p["G"], p["C"], p["K"]
+    xs, ws, _, ys = ref.shapes(p)
+    rng = np.random.default_rng(78)
+    x, w, dy = rng.standard_normal(xs), rng.standard_normal(ws), rng.standard_normal(ys)
+    xt = torch.from_numpy(x).reshape(N, *p["in"], G * C).permute(0, 4, 1, 2, 3).contiguous().requires_grad_(True)
+    wt = torch.from_numpy(w).reshape(G * K, *p["filt"], C).permute(0, 4, 1, 2, 3).contiguous().requires_grad_(True)
+    yt = F.conv3d(xt, wt, None, stride=p["stride"], padding=p["pad"], dilation=p["dil"], groups=G)
+    dyt = torch.from_numpy(dy).reshape(N, *ys[1:4], G * K).permute(0, 4, 1, 2, 3).contiguous()
+    yt.backward(dyt)
+    dx_t = xt.grad.permute(0, 2, 3, 4, 1).reshape(xs).numpy()
+    dw_t = wt.grad.permute(0, 2, 3, 4, 1).reshape(ws).numpy()
+    dx, _ = ref.conv_bwd_data(p, dy, w)
+    dw, _ = ref.conv_bwd_weight(p, x, dy)
+    assert np.max(np.abs(dx - dx_t)) <= 1e-12 * max(1.0, np.max(np.abs(dx_t)))
+    assert np.max(np.abs(dw - dw_t)) <= 1e-12 * max(1.0, np.max(np.abs(dw_t)))
+
+
+@pytest.mark.parametrize("p,t0", [
+    (sd.conv1d_problem(2, 4, 6, 17, 5, 2, 3, 2), (0, 0, 3)),
+    (sd.problem(1, 1, 3, 5, (5, 6, 7), (3, 2, 3), (2, 1, 1), (2, 1, 1), (2, 1, 2)), (2, 0, 1)),
+])
+def test_backward_data_of_a_delta_kernel_scatters_dy(p, t0):
+    """w[g,k,t,c] = 1 iff c == k mod C and t == t0: each dy[o,k] lands on
+    dx[o*s - p + t0*d, k mod C] (dropped in the padding), summed over the k
+    that share a channel -- exact in any dtype."""
+    xs, ws, _, ys = ref.shapes(p)
+    dy = np.random.default_rng(11).integers(-3, 4, ys).astype(np.float64)
+    G, C, K = p["G"], p["C"], p["K"]
+    w = np.zeros(ws)
+    for k in range(K):
+        w[:, k, t0[0], t0[1], t0[2], k % C] = 1.0
+    dx, _ = ref.conv_bwd_data(p, dy, w)
+    exp = np.zeros(xs)
+    Do, Ho, Wo = ref.out_dims(p)
+    for n, od, oh, ow in itertools.product(range(p["N"]), range(Do), range(Ho), range(Wo)):
+        pos = [o * s - q + t * d for o, s, q, t, d in zip((od, oh, ow), p["stride"], p["pad"], t0, p["dil"])]
+        if all(0 <= v < I for v, I in zip(pos, p["in"])):
+            for k in range(K):
+                exp[n, pos[0], pos[1], pos[2], :, k % C] += dy[n, od, oh, ow, :, k]
+    assert np.array_equal(dx, exp)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_backward_weight_all_ones_counts_valid_outputs(wid):
+    """All-ones x and dy: dw[g,k,t,c] = N * prod_d (number of outputs o_d whose
+    tap t_d lands inside the input), at the configured grouped shapes (batch
+    cut to 1)."""
+    p = dict(sd.layers(wid)[0][0], N=1)
+    xs, ws, _, ys = ref.shapes(p)
+    dw, _ = ref.conv_bwd_weight(p, np.ones(xs), np.ones(ys))
+    O = ref.out_dims(p)
+    cnt = [np.array([sum(1 for o in range(O[i]) if 0 <= o * p["stride"][i] - p["pad"][i] + t * p["dil"][i] < p["in"][i])
+                     for t in range(p["filt"][i])]) for i in range(3)]
+    exp = p["N"] * cnt[0][:, None, None] * cnt[1][None, :, None] * cnt[2][None, None, :]
+    assert np.array_equal(dw, np.broadcast_to(exp[None, None, :, :, :, None], dw.shape))
+
+
+def test_backward_points_equal_full_outputs():
+    p = sd.problem(2, 3, 4, 5, (3, 5, 6), (2, 3, 2), (1, 2, 2), (1, 1, 0), (1, 1, 2))
+    xs, ws, _, ys = ref.shapes(p)
+    rng = np.random.default_rng(3)
+    x, w, dy = rng.standard_normal(xs), rng.standard_normal(ws), rng.standard_normal(ys)
+    dx, adx = ref.conv_bwd_data(p, dy, w)
+    dw, adw = ref.conv_bwd_weight(p, x, dy)
+    ix = rng.integers(0, dx.size, 200)
+    iw = rng.integers(0, dw.size, 200)
+    v, a = ref.conv_bwd_data_points(p, dy, w, ix)
+    assert np.array_equal(v, dx.ravel()[ix]) and np.array_equal(a, adx.ravel()[ix])
+    v, a = ref.conv_bwd_weight_points(p, x, dy, iw)
+    assert np.array_equal(v, dw.ravel()[iw]) and np.array_equal(a, adw.ravel()[iw])
