@@ -17,11 +17,13 @@ ConvChain(first, second, "bf16", has_bias, gelu) runs two 1-D convs back to
 back in one kernel (the conv frontend), the intermediate kept on chip;
 ConvChain.pack(w1, w2) prepacks the weights once and ConvChain.run_packed
 runs the chain from them.
+
+ConvBwdData(problem, dtype) is the input gradient of a forward problem.
 """
 from . import capi
 from .capi import ConvError  # noqa: F401
 
-__all__ = ["ConvFwd", "ConvChain", "ConvError", "capi", "desc_from_problem"]
+__all__ = ["ConvFwd", "ConvChain", "ConvBwdData", "ConvError", "capi", "desc_from_problem"]
 
 
 def _ndim(p):
@@ -246,4 +248,57 @@ class ConvChain:
         else:
             capi.conv_chain_run_packed_events(self._plan, xp, packed.data_ptr(), b1p, b2p, yp, s.cuda_stream,
                                               events[0].cuda_event, events[1].cuda_event)
+        return out
+
+
+class ConvBwdData:
+    """Input gradient of a forward convolution problem (conv_bwd_data_*):
+    dx = the gradient of <conv(x, w), dy> with respect to x.  `problem` is
+    the forward problem; no bias or GELU.  The workspace it needs is
+    allocated once here (torch, caller-side) and reused by every call."""
+
+    def __init__(self, problem, dtype):
+        self.problem = dict(problem)
+        self.dtype = dtype
+        self._plan = capi.conv_bwd_data_create(desc_from_problem(problem, dtype, False, False))
+        fwd = ConvFwd(problem, dtype)
+        self.dy_shape, self.w_shape, self.dx_shape = fwd.y_shape, fwd.w_shape, fwd.x_shape
+        self._flop = fwd.useful_flop()
+        fwd.close()
+        self.workspace_bytes = capi.conv_bwd_data_workspace_bytes(self._plan)
+        self._ws = None
+
+    def useful_flop(self):
+        """2 * multiply-adds of the gradient sum: the forward's count."""
+        return self._flop
+
+    def describe(self):
+        return capi.conv_bwd_data_describe(self._plan)
+
+    def close(self):
+        if getattr(self, "_plan", None):
+            capi.conv_bwd_data_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __call__(self, dy, w, out=None, stream=None, workspace=None):
+        import torch
+        tdt = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        for t, shape, name in ((dy, self.dy_shape, "dy"), (w, self.w_shape, "w")):
+            if t.device.type != "cuda" or t.dtype != tdt or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError("%s must be a contiguous cuda %s tensor of shape %r" % (name, tdt, shape))
+        if out is None:
+            out = torch.empty(self.dx_shape, dtype=tdt, device=dy.device)
+        if workspace is None:
+            if self._ws is None or self._ws.device != dy.device:
+                self._ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=dy.device)
+            workspace = self._ws
+        s = stream if stream is not None else torch.cuda.current_stream(dy.device)
+        capi.conv_bwd_data_run(self._plan, dy.data_ptr(), w.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                               workspace.numel(), s.cuda_stream)
         return out

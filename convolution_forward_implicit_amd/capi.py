@@ -29,7 +29,8 @@ EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims
             "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error",
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
             "conv_chain_describe", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
-            "conv_chain_run_packed_events"]
+            "conv_chain_run_packed_events", "conv_bwd_data_create", "conv_bwd_data_workspace_bytes",
+            "conv_bwd_data_run", "conv_bwd_data_destroy", "conv_bwd_data_describe"]
 
 
 class conv_fwd_desc_t(ctypes.Structure):
@@ -102,6 +103,16 @@ def lib():
         L.conv_chain_run_packed.restype = ctypes.c_int
         L.conv_chain_run_packed_events.argtypes = [P] * 9
         L.conv_chain_run_packed_events.restype = ctypes.c_int
+        L.conv_bwd_data_create.argtypes = [D, ctypes.POINTER(P)]
+        L.conv_bwd_data_create.restype = ctypes.c_int
+        L.conv_bwd_data_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_bwd_data_workspace_bytes.restype = ctypes.c_int
+        L.conv_bwd_data_run.argtypes = [P, P, P, P, P, ctypes.c_int64, P]
+        L.conv_bwd_data_run.restype = ctypes.c_int
+        L.conv_bwd_data_destroy.argtypes = [P]
+        L.conv_bwd_data_destroy.restype = None
+        L.conv_bwd_data_describe.argtypes = [P]
+        L.conv_bwd_data_describe.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -210,6 +221,30 @@ def conv_chain_run_packed(plan, x, packed, b1, b2, y, stream=0):
 
 def conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream=0, start_event=None, stop_event=None):
     _check(lib().conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream, start_event, stop_event))
+
+
+def conv_bwd_data_create(desc):
+    plan = ctypes.c_void_p()
+    _check(lib().conv_bwd_data_create(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan.value
+
+
+def conv_bwd_data_workspace_bytes(plan):
+    n = ctypes.c_int64()
+    _check(lib().conv_bwd_data_workspace_bytes(plan, ctypes.byref(n)))
+    return n.value
+
+
+def conv_bwd_data_run(plan, dy, w, dx, workspace, workspace_bytes, stream=0):
+    _check(lib().conv_bwd_data_run(plan, dy, w, dx, workspace, int(workspace_bytes), stream))
+
+
+def conv_bwd_data_destroy(plan):
+    lib().conv_bwd_data_destroy(plan)
+
+
+def conv_bwd_data_describe(plan):
+    return lib().conv_bwd_data_describe(plan).decode()
 
 
 def conv_fwd_last_error():

@@ -27,6 +27,7 @@
 #include "patch_kernel.h"
 #include "chain_kernel.h"
 #include "chain_packed.h"
+#include "bwd_kernels.h"
 
 namespace convfwd {
 namespace {
@@ -304,6 +305,16 @@ struct conv_chain_plan {
     int pgrid;
     int64_t packed_bytes;   // 0: C1 beyond what the prepacked kernel supports
     char text[320];
+};
+
+struct conv_bwd_data_plan {
+    conv_fwd_desc_t desc;     // the forward problem
+    conv_fwd_plan_t *fwd;     // dx = forward conv of (dyp or dy) with w'
+    bool spread;              // build the zero-inserted copy of dy
+    SpreadParams sp;          // pointers filled per run
+    int64_t dy_elems, w_elems, dx_elems;
+    int64_t ws_wt, ws_dyp, ws_bytes;   // workspace: w' at 0, dyp at ws_wt
+    char text[400];
 };
 
 struct conv_fwd_plan {
@@ -823,6 +834,151 @@ conv_status_t conv_chain_run_packed(const conv_chain_plan_t *plan, const void *x
 }
 
 void conv_chain_destroy(conv_chain_plan_t *plan) { delete plan; }
+
+// ---- Backward-data ---------------------------------------------------------
+conv_status_t conv_bwd_data_create(const conv_fwd_desc_t *desc, conv_bwd_data_plan_t **plan)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    *plan = nullptr;
+    int64_t o[3];
+    conv_status_t st = validate(desc, o);
+    if (st != CONV_OK) return st;
+    const conv_fwd_desc_t &d = *desc;
+    if (d.has_bias || d.gelu)
+        return fail(CONV_ERR_UNSUPPORTED, "backward of the linear convolution only: has_bias and gelu must be 0");
+    const int64_t esz = d.dtype == CONV_DT_BF16 ? 2 : 4;
+    conv_bwd_data_plan *pl = new (std::nothrow) conv_bwd_data_plan();
+    if (!pl) return fail(CONV_ERR_NOMEM, "plan allocation failed");
+    pl->desc = d;
+    bool unit = true;
+    int64_t off[3], P[3];
+    for (int i = 0; i < 3; ++i) {
+        off[i] = d.dilation[i] * (d.filt[i] - 1) - d.pad[i];
+        P[i] = d.in[i] + d.dilation[i] * (d.filt[i] - 1);
+        unit = unit && d.stride[i] == 1 && off[i] >= 0;
+    }
+    pl->spread = !unit;
+    conv_fwd_desc_t f = d;   // dx = conv(dyp, w'): K input channels, C output channels
+    f.C = d.K;
+    f.K = d.C;
+    for (int i = 0; i < 3; ++i) {
+        f.stride[i] = 1;
+        f.in[i] = unit ? o[i] : P[i];
+        f.pad[i] = unit ? off[i] : 0;
+    }
+    st = conv_fwd_create(&f, &pl->fwd);
+    if (st != CONV_OK) {
+        delete pl;
+        return st;
+    }
+    int64_t fo[3];
+    conv_fwd_out_dims(pl->fwd, fo);
+    if (fo[0] != d.in[0] || fo[1] != d.in[1] || fo[2] != d.in[2]) {   // cannot happen: extents of the rewrite
+        conv_fwd_destroy(pl->fwd);
+        delete pl;
+        return fail(CONV_ERR_HIP, "internal: backward-data rewrite has the wrong extent");
+    }
+    pl->dy_elems = d.N * o[0] * o[1] * o[2] * d.G * d.K;
+    pl->w_elems = d.G * d.K * d.filt[0] * d.filt[1] * d.filt[2] * d.C;
+    pl->dx_elems = d.N * d.in[0] * d.in[1] * d.in[2] * d.G * d.C;
+    pl->ws_wt = (pl->w_elems * esz + 255) / 256 * 256;
+    pl->ws_dyp = 0;
+    if (pl->spread) {
+        const double dyp = (double)d.N * P[0] * P[1] * P[2] * d.G * d.K;
+        if (dyp * esz >= 2147483647.0) {
+            conv_fwd_destroy(pl->fwd);
+            delete pl;
+            return fail(CONV_ERR_UNSUPPORTED, "backward-data: the spread copy of dy would be 2 GiB or more");
+        }
+        pl->ws_dyp = (int64_t)dyp * esz;
+        SpreadParams &sp = pl->sp;
+        sp.N = (int)d.N;
+        sp.G = (int)d.G;
+        sp.KB = (int)(d.K * esz);
+        for (int i = 0; i < 3; ++i) {
+            sp.O[i] = (int)o[i];
+            sp.P[i] = (int)P[i];
+            sp.s[i] = (int)d.stride[i];
+            sp.off[i] = (int)off[i];
+        }
+    }
+    pl->ws_bytes = pl->ws_wt + pl->ws_dyp;
+    snprintf(pl->text, sizeof(pl->text), "bwd_data %s via %s: %s", d.dtype == CONV_DT_BF16 ? "bf16" : "f32",
+             pl->spread ? "spread dy + flipped weights" : "padded dy + flipped weights", conv_fwd_describe(pl->fwd));
+    if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
+    *plan = pl;
+    return CONV_OK;
+}
+
+conv_status_t conv_bwd_data_workspace_bytes(const conv_bwd_data_plan_t *plan, int64_t *bytes)
+{
+    if (!plan || !bytes) return fail(CONV_ERR_INVALID_ARG, "plan or bytes is NULL");
+    *bytes = plan->ws_bytes;
+    return CONV_OK;
+}
+
+conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy, const void *w, void *dx,
+                                void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    if (!w) return fail(CONV_ERR_INVALID_ARG, "w is NULL");
+    if (plan->dx_elems == 0) return CONV_OK;
+    if (!dy || !dx || !workspace) return fail(CONV_ERR_INVALID_ARG, "dy, dx or workspace is NULL");
+    if (workspace_bytes < plan->ws_bytes)
+        return fail(CONV_ERR_INVALID_ARG, "workspace has %lld bytes, the plan needs %lld", (long long)workspace_bytes,
+                    (long long)plan->ws_bytes);
+    if (((uintptr_t)dy | (uintptr_t)w | (uintptr_t)dx | (uintptr_t)workspace) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "dy, w, dx and workspace must be 16-byte aligned");
+    const int64_t esz = plan->desc.dtype == CONV_DT_BF16 ? 2 : 4;
+    const int64_t dxb = plan->dx_elems * esz;
+    if (overlaps(dx, dxb, dy, plan->dy_elems * esz) || overlaps(dx, dxb, w, plan->w_elems * esz) ||
+        overlaps(dx, dxb, workspace, plan->ws_bytes))
+        return fail(CONV_ERR_INVALID_ARG, "dx overlaps dy, w or the workspace");
+    if (overlaps(workspace, plan->ws_bytes, dy, plan->dy_elems * esz) ||
+        overlaps(workspace, plan->ws_bytes, w, plan->w_elems * esz))
+        return fail(CONV_ERR_INVALID_ARG, "the workspace overlaps dy or w");
+    const conv_fwd_desc_t &d = plan->desc;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
+    (void)hipGetLastError();
+    const int64_t wb = (plan->w_elems + 255) / 256;
+    if (d.dtype == CONV_DT_BF16)
+        hipLaunchKernelGGL(bwd_data_weights_kernel<uint16_t>, dim3((unsigned)wb), dim3(256), 0, s,
+                           (const uint16_t *)w, (uint16_t *)ws, (int)d.K, (int)d.C, (int)d.filt[0], (int)d.filt[1],
+                           (int)d.filt[2], plan->w_elems);
+    else
+        hipLaunchKernelGGL(bwd_data_weights_kernel<float>, dim3((unsigned)wb), dim3(256), 0, s, (const float *)w,
+                           (float *)ws, (int)d.K, (int)d.C, (int)d.filt[0], (int)d.filt[1], (int)d.filt[2],
+                           plan->w_elems);
+    const void *src = dy;
+    if (plan->spread) {
+        SpreadParams sp = plan->sp;
+        sp.dy = dy;
+        sp.dyp = ws + plan->ws_wt;
+        const int vb = sp.KB % 16 == 0 ? 16 : sp.KB % 4 == 0 ? 4 : 2;
+        sp.total = plan->ws_dyp / vb;
+        const dim3 g((unsigned)((sp.total + 255) / 256));
+        if (vb == 16)
+            hipLaunchKernelGGL(bwd_data_spread_kernel<uint4>, g, dim3(256), 0, s, sp);
+        else if (vb == 4)
+            hipLaunchKernelGGL(bwd_data_spread_kernel<uint32_t>, g, dim3(256), 0, s, sp);
+        else
+            hipLaunchKernelGGL(bwd_data_spread_kernel<uint16_t>, g, dim3(256), 0, s, sp);
+        src = sp.dyp;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return conv_fwd_run(plan->fwd, src, ws, nullptr, dx, stream);
+}
+
+void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan)
+{
+    if (!plan) return;
+    conv_fwd_destroy(plan->fwd);
+    delete plan;
+}
+
+const char *conv_bwd_data_describe(const conv_bwd_data_plan_t *plan) { return plan ? plan->text : ""; }
 
 const char *conv_chain_describe(const conv_chain_plan_t *plan) { return plan ? plan->text : ""; }
 

@@ -211,6 +211,36 @@ void conv_chain_destroy(conv_chain_plan_t *plan);
 /* Description of the chain plan; owned by the plan.  "" for NULL. */
 const char *conv_chain_describe(const conv_chain_plan_t *plan);
 
+/* ---- Backward-data (input gradient) --------------------------------------
+ * The grouped bwd_data convolution that the Composable Kernel grouped-conv
+ * note (section 6) names beside the forward one, same layouts:
+ *
+ *   dx[n,i,g,c] = sum over taps t and k of dy[n,o,g,k] * w[g,k,t,c]
+ *                 for every output o with o*s - p + t*d = i (per spatial dim)
+ *
+ * i.e. the gradient of the forward sum with respect to x (no bias, no GELU:
+ * the backward of the linear convolution).  `desc` describes the FORWARD
+ * problem; has_bias and gelu must be 0 (else CONV_ERR_UNSUPPORTED).  Layouts:
+ * dy as the forward y (N x Do x Ho x Wo x G x K), w as the forward w
+ * (G x K x Z x Y x X x C), dx as the forward x (N x Di x Hi x Wi x G x C);
+ * all in the descriptor's dtype, fp32 sums.
+ *
+ * It runs as a forward convolution (same tile kernels and selector) of dy
+ * spread onto a grid of Di + dd(Z-1) (etc.) positions with tap-flipped,
+ * channel-swapped weights, both written to a caller-owned device workspace
+ * of conv_bwd_data_workspace_bytes bytes (16-byte aligned; with unit strides
+ * and pad <= d(F-1) only the weights).  The library allocates nothing.
+ * Ownership, threading and asynchrony as conv_fwd; errors as conv_fwd_create
+ * and conv_fwd_run, plus INVALID_ARG for a workspace that is NULL, too small
+ * or overlapping dy, w or dx. */
+typedef struct conv_bwd_data_plan conv_bwd_data_plan_t;   /* opaque */
+conv_status_t conv_bwd_data_create(const conv_fwd_desc_t *desc, conv_bwd_data_plan_t **plan);
+conv_status_t conv_bwd_data_workspace_bytes(const conv_bwd_data_plan_t *plan, int64_t *bytes);
+conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy, const void *w, void *dx,
+                                void *workspace, int64_t workspace_bytes, void *stream);
+void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan);
+const char *conv_bwd_data_describe(const conv_bwd_data_plan_t *plan);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *conv_fwd_last_error(void);
 

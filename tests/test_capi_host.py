@@ -17,7 +17,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(conv_(?:fwd|chain)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(conv_(?:fwd|chain|bwd_data|bwd_weight)_\w+)\s*\(", text)))
 
 
 def test_header_declares_what_binding_expects():
@@ -350,3 +350,51 @@ def test_chain_packed_rejects_wide_input_and_bad_arguments():
             capi.conv_chain_packed_bytes(None)
     finally:
         capi.conv_chain_destroy(plan)
+
+
+# --------------------------------------------------------------------------
+# Backward-data: plan-time validation and argument checks (no GPU work)
+def test_bwd_data_create_workspace_and_describe():
+    # unit stride, pad <= d(F-1): only the flipped weights in the workspace
+    p = sd.problem(8, 4, 64, 64, (1, 56, 56), (1, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1))
+    plan = capi.conv_bwd_data_create(desc_from_problem(p, "bf16"))
+    try:
+        assert capi.conv_bwd_data_workspace_bytes(plan) == (4 * 64 * 9 * 64 * 2 + 255) // 256 * 256
+        assert "padded dy" in capi.conv_bwd_data_describe(plan)
+    finally:
+        capi.conv_bwd_data_destroy(plan)
+    # stride 2: the spread copy of dy (N x (L + 2) x K) follows the weights
+    p = sd.conv1d_problem(32, 384, 384, 3000, 3, 2, 1)
+    plan = capi.conv_bwd_data_create(desc_from_problem(p, "f32"))
+    try:
+        wt = (384 * 3 * 384 * 4 + 255) // 256 * 256
+        assert capi.conv_bwd_data_workspace_bytes(plan) == wt + 32 * 3002 * 384 * 4
+        assert "spread dy" in capi.conv_bwd_data_describe(plan)
+    finally:
+        capi.conv_bwd_data_destroy(plan)
+    capi.conv_bwd_data_destroy(None)
+    assert capi.conv_bwd_data_describe(None) == ""
+
+
+def test_bwd_data_rejects_epilogues_and_bad_arguments():
+    p = sd.problem(2, 2, 16, 8, (1, 9, 9), (1, 3, 3), (1, 2, 2), (0, 1, 1), (1, 1, 1))
+    for hb, ge in ((1, 0), (0, 1)):
+        with pytest.raises(ConvError) as e:
+            capi.conv_bwd_data_create(desc_from_problem(p, "bf16", hb, ge))
+        assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+    plan = capi.conv_bwd_data_create(desc_from_problem(p, "bf16"))
+    try:
+        ws = capi.conv_bwd_data_workspace_bytes(plan)
+        base = 1 << 30
+        for args in ((None, 4096, base, base + (1 << 24), ws),            # dy NULL
+                     (4096, 8192, base, None, ws),                       # workspace NULL
+                     (4096, 8192, base, base + (1 << 24), ws - 16),      # workspace too small
+                     (4096 + 8, 8192, base, base + (1 << 24), ws),       # misaligned
+                     (4096, 8192, base, base + 16, ws)):                 # workspace overlaps dx
+            with pytest.raises(ConvError) as e:
+                capi.conv_bwd_data_run(plan, *args)
+            assert e.value.status == capi.CONV_ERR_INVALID_ARG, e.value.message
+        with pytest.raises(ConvError):
+            capi.conv_bwd_data_run(None, 4096, 8192, base, base + (1 << 24), ws)
+    finally:
+        capi.conv_bwd_data_destroy(plan)

@@ -370,3 +370,95 @@ def test_chain_empty_batch(dev):
     y = e(c.y_shape)
     assert c(e(c.x_shape), e(c.w1_shape), None, e(c.w2_shape), None, out=y) is y
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# Backward-data (conv_bwd_data_*): dx against the oracle's input gradient.
+# The device sums taps * K terms per element (the rewrite as a forward conv
+# adds the zero taps), so the bound's n is that count.
+BWD = [
+    ("conv1d_s2", sd.conv1d_problem(2, 64, 48, 301, 3, 2, 1)),
+    ("grouped2d_s1", sd.problem(2, 4, 16, 8, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1))),
+    ("grouped2d_s2_dil", sd.problem(2, 2, 16, 24, (1, 13, 11), (1, 3, 3), (1, 2, 2), (0, 1, 2), (1, 1, 2))),
+    ("grouped3d_dil2", sd.problem(1, 8, 32, 32, (6, 9, 9), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2))),
+    ("pad_wider_than_filter", sd.conv1d_problem(2, 8, 8, 20, 3, 1, 3)),
+    ("odd_channels_s2", sd.conv1d_problem(3, 3, 5, 77, 5, 2, 2)),
+    ("stride_gt_filter", sd.problem(2, 1, 16, 8, (1, 17, 19), (1, 2, 2), (1, 3, 3), (0, 0, 1))),
+    ("mixed_3d", sd.problem(1, 2, 5, 3, (4, 5, 7), (2, 1, 3), (2, 1, 3), (1, 0, 1), (1, 1, 1))),
+]
+
+
+def _terms(n):
+    """A stand-in problem whose reduction length (the bound's n) is n."""
+    return {"C": int(n), "filt": (1, 1, 1)}
+
+
+def _dy(p, dtype, seed, kind):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ys = ref.shapes(p)[3]
+    if kind == "int":
+        return rng.integers(-2, 3, size=ys).astype(np.float32)
+    v = rng.uniform(-1.0, 1.0, size=ys).astype(np.float32)
+    return sd.round_bf16(v) if dtype == "bf16" else v
+
+
+def run_bwd_data(dev, p, dtype, dy, w):
+    from convolution_forward_implicit_amd import ConvBwdData
+    c = ConvBwdData(p, dtype)
+    print("case: bwd_data", p, dtype, c.describe(), flush=True)
+    dx = c(to_dev(dy, dtype, dev), to_dev(w, dtype, dev))
+    torch.cuda.synchronize()
+    return dx, c
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,p", BWD, ids=[b[0] for b in BWD])
+def test_bwd_data_integer_bit_exact(dev, name, p, dt):
+    _, w, _ = sd.random_inputs(p, dt, 91, False, kind="int")
+    dy = _dy(p, dt, 92, "int")
+    dx, _ = run_bwd_data(dev, p, dt, dy, w)
+    r, _ = ref.conv_bwd_data(p, dy, w)
+    if dt == "f32":
+        assert np.array_equal(host(dx), r)
+    else:
+        assert np.array_equal(bits(dx).ravel(), check.round_to_bf16_bits(r).ravel())
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("name,p", BWD, ids=[b[0] for b in BWD])
+def test_bwd_data_seeded_float_parity(dev, name, p, dt):
+    _, w, _ = sd.random_inputs(p, dt, 93, False)
+    dy = _dy(p, dt, 94, "float")
+    dx, _ = run_bwd_data(dev, p, dt, dy, w)
+    r, a = ref.conv_bwd_data(p, dy, w)
+    st = check.check(host(dx), r, a, _terms(p["K"] * np.prod(p["filt"])), dt, False, False)
+    print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_bwd_data_grouped_workloads_full_size_sampled(dev, wid):
+    """The grouped 2-D and dilated 3-D workload shapes at full size: 4000
+    random input-gradient elements plus borders against the oracle."""
+    W = sd.workload(wid)
+    (p, _, _), = W["layers"]
+    dy = _dy(p, "bf16", 95, "float")
+    dx, _ = run_bwd_data(dev, p, "bf16", dy, W["w"][0])
+    xs = ref.shapes(p)[0]
+    rng = np.random.Generator(np.random.PCG64(96))
+    idx = np.unique(np.concatenate([rng.integers(0, int(np.prod(xs)), 4000),
+                                    np.arange(0, int(np.prod(xs)), int(np.prod(xs)) // 97)]))
+    r, a = ref.conv_bwd_data_points(p, dy, W["w"][0], idx)
+    st = check.check(host(dx).ravel()[idx], r, a, _terms(p["K"] * np.prod(p["filt"])), "bf16", False, False)
+    print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
+
+
+def test_bwd_data_empty_batch(dev):
+    from convolution_forward_implicit_amd import ConvBwdData
+    p = sd.conv1d_problem(0, 8, 8, 20, 3, 2, 1)
+    c = ConvBwdData(p, "f32")
+    dx = torch.empty(c.dx_shape, dtype=torch.float32, device=dev)
+    assert c(torch.empty(c.dy_shape, dtype=torch.float32, device=dev),
+             torch.empty(c.w_shape, dtype=torch.float32, device=dev), out=dx) is dx
+    torch.cuda.synchronize()
