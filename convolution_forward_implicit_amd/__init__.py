@@ -18,12 +18,13 @@ back in one kernel (the conv frontend), the intermediate kept on chip;
 ConvChain.pack(w1, w2) prepacks the weights once and ConvChain.run_packed
 runs the chain from them.
 
-ConvBwdData(problem, dtype) is the input gradient of a forward problem.
+ConvBwdData(problem, dtype) is the input gradient of a forward problem,
+ConvBwdWeight(problem) its weight gradient (bf16).
 """
 from . import capi
 from .capi import ConvError  # noqa: F401
 
-__all__ = ["ConvFwd", "ConvChain", "ConvBwdData", "ConvError", "capi", "desc_from_problem"]
+__all__ = ["ConvFwd", "ConvChain", "ConvBwdData", "ConvBwdWeight", "ConvError", "capi", "desc_from_problem"]
 
 
 def _ndim(p):
@@ -301,4 +302,55 @@ class ConvBwdData:
         s = stream if stream is not None else torch.cuda.current_stream(dy.device)
         capi.conv_bwd_data_run(self._plan, dy.data_ptr(), w.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                workspace.numel(), s.cuda_stream)
+        return out
+
+
+class ConvBwdWeight:
+    """Weight gradient of a forward convolution problem (conv_bwd_weight_*):
+    dw = the gradient of <conv(x, w), dy> with respect to w, bf16.  The
+    workspace it needs is allocated once here (torch, caller-side)."""
+
+    def __init__(self, problem, dtype="bf16"):
+        self.problem = dict(problem)
+        self.dtype = dtype
+        self._plan = capi.conv_bwd_weight_create(desc_from_problem(problem, dtype, False, False))
+        fwd = ConvFwd(problem, dtype)
+        self.x_shape, self.dy_shape, self.dw_shape = fwd.x_shape, fwd.y_shape, fwd.w_shape
+        self._flop = fwd.useful_flop()
+        fwd.close()
+        self.workspace_bytes = capi.conv_bwd_weight_workspace_bytes(self._plan)
+        self._ws = None
+
+    def useful_flop(self):
+        """2 * multiply-adds of the gradient sum: the forward's count."""
+        return self._flop
+
+    def describe(self):
+        return capi.conv_bwd_weight_describe(self._plan)
+
+    def close(self):
+        if getattr(self, "_plan", None):
+            capi.conv_bwd_weight_destroy(self._plan)
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __call__(self, x, dy, out=None, stream=None, workspace=None):
+        import torch
+        for t, shape, name in ((x, self.x_shape, "x"), (dy, self.dy_shape, "dy")):
+            if t.device.type != "cuda" or t.dtype != torch.bfloat16 or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError("%s must be a contiguous cuda bfloat16 tensor of shape %r" % (name, shape))
+        if out is None:
+            out = torch.empty(self.dw_shape, dtype=torch.bfloat16, device=x.device)
+        if workspace is None:
+            if self._ws is None or self._ws.device != x.device:
+                self._ws = torch.empty(max(self.workspace_bytes, 16), dtype=torch.uint8, device=x.device)
+            workspace = self._ws
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        capi.conv_bwd_weight_run(self._plan, x.data_ptr(), dy.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), s.cuda_stream)
         return out

@@ -30,7 +30,9 @@ EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
             "conv_chain_describe", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
             "conv_chain_run_packed_events", "conv_bwd_data_create", "conv_bwd_data_workspace_bytes",
-            "conv_bwd_data_run", "conv_bwd_data_destroy", "conv_bwd_data_describe"]
+            "conv_bwd_data_run", "conv_bwd_data_destroy", "conv_bwd_data_describe", "conv_bwd_weight_create",
+            "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_run", "conv_bwd_weight_destroy",
+            "conv_bwd_weight_describe"]
 
 
 class conv_fwd_desc_t(ctypes.Structure):
@@ -113,6 +115,16 @@ def lib():
         L.conv_bwd_data_destroy.restype = None
         L.conv_bwd_data_describe.argtypes = [P]
         L.conv_bwd_data_describe.restype = ctypes.c_char_p
+        L.conv_bwd_weight_create.argtypes = [D, ctypes.POINTER(P)]
+        L.conv_bwd_weight_create.restype = ctypes.c_int
+        L.conv_bwd_weight_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_bwd_weight_workspace_bytes.restype = ctypes.c_int
+        L.conv_bwd_weight_run.argtypes = [P, P, P, P, P, ctypes.c_int64, P]
+        L.conv_bwd_weight_run.restype = ctypes.c_int
+        L.conv_bwd_weight_destroy.argtypes = [P]
+        L.conv_bwd_weight_destroy.restype = None
+        L.conv_bwd_weight_describe.argtypes = [P]
+        L.conv_bwd_weight_describe.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -245,6 +257,30 @@ def conv_bwd_data_destroy(plan):
 
 def conv_bwd_data_describe(plan):
     return lib().conv_bwd_data_describe(plan).decode()
+
+
+def conv_bwd_weight_create(desc):
+    plan = ctypes.c_void_p()
+    _check(lib().conv_bwd_weight_create(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan.value
+
+
+def conv_bwd_weight_workspace_bytes(plan):
+    n = ctypes.c_int64()
+    _check(lib().conv_bwd_weight_workspace_bytes(plan, ctypes.byref(n)))
+    return n.value
+
+
+def conv_bwd_weight_run(plan, x, dy, dw, workspace, workspace_bytes, stream=0):
+    _check(lib().conv_bwd_weight_run(plan, x, dy, dw, workspace, int(workspace_bytes), stream))
+
+
+def conv_bwd_weight_destroy(plan):
+    lib().conv_bwd_weight_destroy(plan)
+
+
+def conv_bwd_weight_describe(plan):
+    return lib().conv_bwd_weight_describe(plan).decode()
 
 
 def conv_fwd_last_error():

@@ -105,6 +105,12 @@ void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStre
         hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, false, false>), g, b, 0, s, e0, e1, 0, pp);
 }
 
+template <int KT, int TT>
+void launch_wgrad(const WgradParams &wp, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((wgrad_kernel<KT, KT, TT>), dim3(grid), dim3(256), 0, s, wp);
+}
+
 enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2 };
 
 struct TileCfg {
@@ -315,6 +321,15 @@ struct conv_bwd_data_plan {
     int64_t dy_elems, w_elems, dx_elems;
     int64_t ws_wt, ws_dyp, ws_bytes;   // workspace: w' at 0, dyp at ws_wt
     char text[400];
+};
+
+struct conv_bwd_weight_plan {
+    conv_fwd_desc_t desc;     // the forward problem
+    WgradParams wp;           // pointers filled per run
+    int KT, TT;               // tile: KT x KT channels, TT taps
+    int grid;
+    int64_t x_elems, dy_elems, dw_elems, ws_bytes;
+    char text[320];
 };
 
 struct conv_fwd_plan {
@@ -979,6 +994,123 @@ void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan)
 }
 
 const char *conv_bwd_data_describe(const conv_bwd_data_plan_t *plan) { return plan ? plan->text : ""; }
+
+// ---- Backward-weight ---------------------------------------------------------
+conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weight_plan_t **plan)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    *plan = nullptr;
+    int64_t o[3];
+    conv_status_t st = validate(desc, o);
+    if (st != CONV_OK) return st;
+    const conv_fwd_desc_t &d = *desc;
+    if (d.has_bias || d.gelu)
+        return fail(CONV_ERR_UNSUPPORTED, "backward of the linear convolution only: has_bias and gelu must be 0");
+    if (d.dtype != CONV_DT_BF16) return fail(CONV_ERR_UNSUPPORTED, "backward-weight: bf16 only");
+    if (d.C % 8 != 0 || d.K % 8 != 0)
+        return fail(CONV_ERR_UNSUPPORTED, "backward-weight: C and K per group must be multiples of 8 (C = %lld, K = %lld)",
+                    (long long)d.C, (long long)d.K);
+    conv_bwd_weight_plan *pl = new (std::nothrow) conv_bwd_weight_plan();
+    if (!pl) return fail(CONV_ERR_NOMEM, "plan allocation failed");
+    pl->desc = d;
+    const int taps = (int)(d.filt[0] * d.filt[1] * d.filt[2]);
+    pl->KT = std::min(d.K, d.C) > 32 ? 64 : 32;
+    const int tmax = pl->KT == 64 ? 9 : 27;     // 32x32 blocks per workgroup <= 36
+    pl->TT = 1;
+    for (int tt : {27, 9, 3})
+        if (tt <= tmax && taps % tt == 0) { pl->TT = tt; break; }
+    WgradParams &wp = pl->wp;
+    wp.N = (int)d.N; wp.G = (int)d.G; wp.C = (int)d.C; wp.K = (int)d.K;
+    wp.Di = (int)d.in[0]; wp.Hi = (int)d.in[1]; wp.Wi = (int)d.in[2];
+    wp.Do = (int)o[0]; wp.Ho = (int)o[1]; wp.Wo = (int)o[2];
+    wp.sd = (int)d.stride[0]; wp.sh = (int)d.stride[1]; wp.sw = (int)d.stride[2];
+    wp.pd = (int)d.pad[0]; wp.ph = (int)d.pad[1]; wp.pw = (int)d.pad[2];
+    wp.dd = (int)d.dilation[0]; wp.dh = (int)d.dilation[1]; wp.dw = (int)d.dilation[2];
+    wp.Y = (int)d.filt[1]; wp.X = (int)d.filt[2]; wp.taps = taps;
+    wp.pixels = d.N * o[0] * o[1] * o[2];
+    wp.fd_Wo = make_fastdiv(wp.Wo); wp.fd_Ho = make_fastdiv(wp.Ho); wp.fd_Do = make_fastdiv(wp.Do);
+    wp.kt_n = (int)((d.K + pl->KT - 1) / pl->KT);
+    wp.ct_n = (int)((d.C + pl->KT - 1) / pl->KT);
+    wp.tg_n = taps / pl->TT;
+    const int64_t tiles = d.G * wp.kt_n * wp.ct_n * wp.tg_n;
+    const int64_t steps = (wp.pixels + 31) / 32;
+    // split the pixels so that about two workgroups per compute unit run
+    int64_t splits = std::max<int64_t>(1, std::min<int64_t>(steps, (2 * device_cu_count() + tiles - 1) / tiles));
+    const int64_t per = std::max<int64_t>(1, (steps + splits - 1) / splits);
+    splits = std::max<int64_t>(1, (steps + per - 1) / per);
+    wp.splits = (int)splits;
+    wp.steps_per_split = (int)per;
+    pl->x_elems = d.N * d.in[0] * d.in[1] * d.in[2] * d.G * d.C;
+    pl->dy_elems = wp.pixels * d.G * d.K;
+    pl->dw_elems = d.G * d.K * taps * d.C;
+    const double grid = (double)tiles * splits;
+    if (grid >= 2147483647.0 || (double)pl->dw_elems * splits >= 2147483647.0 * 4) {
+        delete pl;
+        return fail(CONV_ERR_UNSUPPORTED, "backward-weight: problem too large");
+    }
+    pl->grid = (int)grid;
+    pl->ws_bytes = pl->dw_elems * splits * 4;
+    snprintf(pl->text, sizeof(pl->text),
+             "bwd_weight bf16 tile %dx%d ch x %d taps, %lld tiles x %d splits of %d x 32 pixels, grid=%d lds=%dB",
+             pl->KT, pl->KT, pl->TT, (long long)tiles, wp.splits, wp.steps_per_split, pl->grid,
+             pl->KT == 64 ? (64 + pl->TT * 64) * 72 : (32 + pl->TT * 32) * 72);
+    if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
+    *plan = pl;
+    return CONV_OK;
+}
+
+conv_status_t conv_bwd_weight_workspace_bytes(const conv_bwd_weight_plan_t *plan, int64_t *bytes)
+{
+    if (!plan || !bytes) return fail(CONV_ERR_INVALID_ARG, "plan or bytes is NULL");
+    *bytes = plan->ws_bytes;
+    return CONV_OK;
+}
+
+conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void *x, const void *dy, void *dw,
+                                  void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    if (!dw || !workspace) return fail(CONV_ERR_INVALID_ARG, "dw or workspace is NULL");
+    if (plan->dy_elems > 0 && (!x || !dy)) return fail(CONV_ERR_INVALID_ARG, "x or dy is NULL");
+    if (workspace_bytes < plan->ws_bytes)
+        return fail(CONV_ERR_INVALID_ARG, "workspace has %lld bytes, the plan needs %lld", (long long)workspace_bytes,
+                    (long long)plan->ws_bytes);
+    if (((uintptr_t)x | (uintptr_t)dy | (uintptr_t)dw | (uintptr_t)workspace) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "x, dy, dw and workspace must be 16-byte aligned");
+    const int64_t dwb = plan->dw_elems * 2;
+    if (overlaps(dw, dwb, x, plan->x_elems * 2) || overlaps(dw, dwb, dy, plan->dy_elems * 2) ||
+        overlaps(dw, dwb, workspace, plan->ws_bytes))
+        return fail(CONV_ERR_INVALID_ARG, "dw overlaps x, dy or the workspace");
+    if (overlaps(workspace, plan->ws_bytes, x, plan->x_elems * 2) ||
+        overlaps(workspace, plan->ws_bytes, dy, plan->dy_elems * 2))
+        return fail(CONV_ERR_INVALID_ARG, "the workspace overlaps x or dy");
+    WgradParams wp = plan->wp;
+    wp.x = x;
+    wp.dy = dy;
+    wp.ws = reinterpret_cast<float *>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (plan->KT == 64) {
+        if (plan->TT == 9) launch_wgrad<64, 9>(wp, plan->grid, s);
+        else if (plan->TT == 3) launch_wgrad<64, 3>(wp, plan->grid, s);
+        else launch_wgrad<64, 1>(wp, plan->grid, s);
+    } else {
+        if (plan->TT == 27) launch_wgrad<32, 27>(wp, plan->grid, s);
+        else if (plan->TT == 9) launch_wgrad<32, 9>(wp, plan->grid, s);
+        else if (plan->TT == 3) launch_wgrad<32, 3>(wp, plan->grid, s);
+        else launch_wgrad<32, 1>(wp, plan->grid, s);
+    }
+    const int64_t n = plan->dw_elems;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const float *)workspace, (uint16_t *)dw, n, wp.splits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+void conv_bwd_weight_destroy(conv_bwd_weight_plan_t *plan) { delete plan; }
+
+const char *conv_bwd_weight_describe(const conv_bwd_weight_plan_t *plan) { return plan ? plan->text : ""; }
 
 const char *conv_chain_describe(const conv_chain_plan_t *plan) { return plan ? plan->text : ""; }
 

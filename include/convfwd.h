@@ -241,6 +241,30 @@ conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy
 void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan);
 const char *conv_bwd_data_describe(const conv_bwd_data_plan_t *plan);
 
+/* ---- Backward-weight (weight gradient) ------------------------------------
+ * The grouped bwd_weight convolution of the same note (section 6):
+ *
+ *   dw[g,k,z,y,x,c] = sum over output pixels (n,od,oh,ow) whose tap (z,y,x)
+ *                     lies inside the input of
+ *                     dy[n,od,oh,ow,g,k] * x[n, od*sd-pd+z*dd, oh*sh-ph+y*dh, ow*sw-pw+x*dw, g, c]
+ *
+ * the gradient of the forward sum with respect to w.  `desc` describes the
+ * FORWARD problem; dtype must be bf16, has_bias and gelu 0, C and K per group
+ * multiples of 8 (else CONV_ERR_UNSUPPORTED).  x, dy, dw in the forward x, y
+ * and w layouts, bf16; sums in fp32 (split over the pixels into fp32
+ * partials in a caller-owned device workspace of
+ * conv_bwd_weight_workspace_bytes bytes, then added in a fixed order, so
+ * results are deterministic) and rounded to bf16 nearest-even.  An empty
+ * batch gives dw = 0.  The library allocates nothing; ownership, threading,
+ * asynchrony and errors as conv_bwd_data. */
+typedef struct conv_bwd_weight_plan conv_bwd_weight_plan_t;   /* opaque */
+conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weight_plan_t **plan);
+conv_status_t conv_bwd_weight_workspace_bytes(const conv_bwd_weight_plan_t *plan, int64_t *bytes);
+conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void *x, const void *dy, void *dw,
+                                  void *workspace, int64_t workspace_bytes, void *stream);
+void conv_bwd_weight_destroy(conv_bwd_weight_plan_t *plan);
+const char *conv_bwd_weight_describe(const conv_bwd_weight_plan_t *plan);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *conv_fwd_last_error(void);
 

@@ -398,3 +398,32 @@ def test_bwd_data_rejects_epilogues_and_bad_arguments():
             capi.conv_bwd_data_run(None, 4096, 8192, base, base + (1 << 24), ws)
     finally:
         capi.conv_bwd_data_destroy(plan)
+
+
+# --------------------------------------------------------------------------
+# Backward-weight: plan-time validation and argument checks (no GPU work)
+def test_bwd_weight_create_and_rejects():
+    p = sd.problem(8, 4, 64, 64, (1, 56, 56), (1, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1))
+    plan = capi.conv_bwd_weight_create(desc_from_problem(p, "bf16"))
+    try:
+        ws = capi.conv_bwd_weight_workspace_bytes(plan)
+        assert ws > 0 and ws % (4 * 64 * 9 * 64 * 4) == 0      # whole fp32 partial tiles per split
+        assert "bwd_weight bf16" in capi.conv_bwd_weight_describe(plan)
+        base = 1 << 30
+        for args in ((4096, 8192, None, base, ws),              # dw NULL
+                     (4096, 8192, base, base + (1 << 24), ws - 4),  # workspace too small
+                     (4096 + 8, 8192, base, base + (1 << 24), ws),  # misaligned
+                     (4096, 8192, base, base + 64, ws)):        # workspace overlaps dw
+            with pytest.raises(ConvError) as e:
+                capi.conv_bwd_weight_run(plan, *args)
+            assert e.value.status == capi.CONV_ERR_INVALID_ARG, e.value.message
+    finally:
+        capi.conv_bwd_weight_destroy(plan)
+    for q, dt in ((p, "f32"), (sd.problem(2, 1, 12, 16, (1, 9, 9), (1, 3, 3)), "bf16")):
+        with pytest.raises(ConvError) as e:
+            capi.conv_bwd_weight_create(desc_from_problem(q, dt))
+        assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+    with pytest.raises(ConvError) as e:
+        capi.conv_bwd_weight_create(desc_from_problem(p, "bf16", 1, 0))
+    assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+    capi.conv_bwd_weight_destroy(None)

@@ -462,3 +462,84 @@ def test_bwd_data_empty_batch(dev):
     assert c(torch.empty(c.dy_shape, dtype=torch.float32, device=dev),
              torch.empty(c.w_shape, dtype=torch.float32, device=dev), out=dx) is dx
     torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------
+# Backward-weight (conv_bwd_weight_*, bf16): dw against the oracle's weight
+# gradient; the device sums N*Do*Ho*Wo terms per element (bound's n).
+WGRAD = [
+    ("conv1d_s2", sd.conv1d_problem(2, 64, 48, 301, 3, 2, 1)),
+    ("grouped2d_s1", sd.problem(2, 4, 16, 8, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1))),
+    ("grouped2d_s2_dil", sd.problem(2, 2, 16, 24, (1, 13, 11), (1, 3, 3), (1, 2, 2), (0, 1, 2), (1, 1, 2))),
+    ("grouped3d_dil2", sd.problem(1, 8, 32, 32, (6, 9, 9), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2))),
+    ("wide_channels_k5", sd.conv1d_problem(1, 96, 80, 200, 5, 1, 2)),
+    ("ragged_tiles", sd.problem(3, 1, 72, 40, (1, 7, 9), (1, 3, 3), (1, 1, 2), (0, 1, 1), (1, 1, 1))),
+    ("pointwise", sd.problem(2, 2, 64, 64, (1, 6, 7), (1, 1, 1))),
+]
+
+
+def run_bwd_weight(dev, p, x, dy):
+    from convolution_forward_implicit_amd import ConvBwdWeight
+    c = ConvBwdWeight(p)
+    print("case: bwd_weight", p, c.describe(), flush=True)
+    dw = c(to_dev(x, "bf16", dev), to_dev(dy, "bf16", dev))
+    torch.cuda.synchronize()
+    return dw, c
+
+
+def _pixels(p):
+    return p["N"] * int(np.prod(ref.out_dims(p)))
+
+
+@pytest.mark.parametrize("name,p", WGRAD, ids=[b[0] for b in WGRAD])
+def test_bwd_weight_integer_bit_exact(dev, name, p):
+    x, _, _ = sd.random_inputs(p, "bf16", 97, False, kind="int")
+    dy = _dy(p, "bf16", 98, "int")
+    dw, _ = run_bwd_weight(dev, p, x, dy)
+    r, _ = ref.conv_bwd_weight(p, x, dy)
+    assert np.array_equal(bits(dw).ravel(), check.round_to_bf16_bits(r).ravel())
+
+
+@pytest.mark.parametrize("name,p", WGRAD, ids=[b[0] for b in WGRAD])
+def test_bwd_weight_seeded_float_parity(dev, name, p):
+    x, _, _ = sd.random_inputs(p, "bf16", 99, False)
+    dy = _dy(p, "bf16", 100, "float")
+    dw, _ = run_bwd_weight(dev, p, x, dy)
+    r, a = ref.conv_bwd_weight(p, x, dy)
+    st = check.check(host(dw), r, a, _terms(_pixels(p)), "bf16", False, False)
+    print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_bwd_weight_grouped_workloads_full_size_sampled(dev, wid):
+    """The grouped workload shapes at full size: 2000 random weight-gradient
+    elements (each a sum over every output pixel) against the oracle."""
+    W = sd.workload(wid)
+    (p, _, _), = W["layers"]
+    dy = _dy(p, "bf16", 101, "float")
+    dw, _ = run_bwd_weight(dev, p, W["x"], dy)
+    ws = ref.shapes(p)[1]
+    idx = np.unique(np.random.Generator(np.random.PCG64(102)).integers(0, int(np.prod(ws)), 2000))
+    r, a = ref.conv_bwd_weight_points(p, W["x"], dy, idx)
+    st = check.check(host(dw).ravel()[idx], r, a, _terms(_pixels(p)), "bf16", False, False)
+    print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
+
+
+def test_bwd_weight_empty_batch_is_zero_and_repeatable(dev):
+    from convolution_forward_implicit_amd import ConvBwdWeight
+    p = sd.conv1d_problem(0, 16, 8, 20, 3, 2, 1)
+    c = ConvBwdWeight(p)
+    dw = torch.full(c.dw_shape, 7.0, dtype=torch.bfloat16, device=dev)
+    c(torch.empty(c.x_shape, dtype=torch.bfloat16, device=dev),
+      torch.empty(c.dy_shape, dtype=torch.bfloat16, device=dev), out=dw)
+    torch.cuda.synchronize()
+    assert float(dw.float().abs().max()) == 0.0
+    # a real problem twice: bitwise the same (fixed-order reduction)
+    q = WGRAD[1][1]
+    x, _, _ = sd.random_inputs(q, "bf16", 103, False)
+    dy = _dy(q, "bf16", 104, "float")
+    a, _ = run_bwd_weight(dev, q, x, dy)
+    b, _ = run_bwd_weight(dev, q, x, dy)
+    assert torch.equal(a, b)
