@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--fused-natural", action="store_true",
                     help="run a two-conv frontend workload as one fused kernel from the natural weights "
                          "(conv_chain_run)")
+    ap.add_argument("--pass", dest="pass_", default="fwd", choices=["fwd", "bwd_data", "bwd_weight"],
+                    help="which pass of the workload's convolutions to time (backward: synthetic dy ~ U[-1,1))")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes --steps times")
     args = ap.parse_args()
@@ -170,6 +172,11 @@ def main():
     esz = 4 if dt == "f32" else 2
     fused = args.fused or args.fused_natural
     prepack = None
+    if args.pass_ != "fwd":
+        if fused:
+            print("bench.py: --fused is a forward path", file=sys.stderr)
+            sys.exit(2)
+        return bench_backward(args, W, dt, tdt, dev, up)
     if fused:
         if len(W["layers"]) != 2:
             print("bench.py: --fused needs a two-conv workload", file=sys.stderr)
@@ -281,6 +288,84 @@ def main():
                    "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU",
                    "weight_prepack": prepack},
         "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_backward(args, W, dt, tdt, dev, up):
+    """Times one backward pass (input or weight gradient) of every layer of
+    the workload: a step is that pass over all layers, on synthetic output
+    gradients dy ~ U[-1, 1) (seeded) and, for the weight gradient of a layer
+    after the first, a synthetic input of that layer's shape.  Each layer's
+    call (its small preparation kernels included) is bracketed by stream
+    events on every --event-every-th step; the roofline entry is the
+    dominant layer's call."""
+    import numpy as np
+    import torch
+    from convolution_forward_implicit_amd import ConvBwdData, ConvBwdWeight
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    rnd = lambda shape: (torch.rand(shape, generator=gen, device=dev) * 2 - 1).to(tdt).contiguous()
+    ops, args_ = [], []
+    for li, (p, _, _) in enumerate(W["layers"]):
+        if args.pass_ == "bwd_data":
+            c = ConvBwdData(p, dt)
+            a = (rnd(c.dy_shape), up(W["w"][li]))
+        else:
+            c = ConvBwdWeight(p, dt)
+            a = (up(W["x"]) if li == 0 else rnd(c.x_shape), rnd(c.dy_shape))
+        ops.append(c)
+        args_.append(a)
+    outs = [None] * len(ops)
+    flops = [c.useful_flop() for c in ops]
+    dom = int(np.argmax(flops))
+
+    def step():
+        for li, c in enumerate(ops):
+            outs[li] = c(*args_[li], out=outs[li], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    E = max(1, args.event_every)
+    lay = [[] for _ in ops]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    evs = []
+    for i in range(K):
+        if i % E == 0:
+            for li, c in enumerate(ops):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                outs[li] = c(*args_[li], out=outs[li], stream=stream)
+                e1.record(stream)
+                evs.append((li, e0, e1))
+        else:
+            step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    for li, e0, e1 in evs:
+        lay[li].append(e0.elapsed_time(e1))
+    dom_ms = float(np.mean(lay[dom]))
+    value = float(sum(flops)) / (ms_step * 1e-3) / 1e12
+    achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS[dt], 4), "traffic": None,
+            "kernel": "layer %d %s (whole call): %s" % (dom + 1, args.pass_, ops[dom].describe()),
+            "kernel_ms": round(dom_ms, 5), "layer_ms": [round(float(np.mean(v)), 5) for v in lay]}
+    line = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": args.workload, "pass": args.pass_, "batch": W["layers"][0][0]["N"],
+                   "layers": [c.describe() for c in ops], "useful_gflop_per_step": round(sum(flops) / 1e9, 4),
+                   "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU"},
+        "roofline": roof, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

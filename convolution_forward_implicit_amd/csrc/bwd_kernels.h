@@ -297,15 +297,19 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
     }
 }
 
-// dw[i] = bf16(sum over splits s, in order, of ws[s][i])
-__global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float *__restrict__ ws, uint16_t *__restrict__ dw,
-                                                           int64_t n, int splits)
+// dw[i] = bf16(sum over splits s, in order, of ws[s][i]), four elements per
+// thread (n4 = elements / 4)
+__global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float4 *__restrict__ ws, uint2 *__restrict__ dw,
+                                                           int64_t n4, int splits)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float s = 0.f;
-    for (int k = 0; k < splits; ++k) s += ws[(int64_t)k * n + i];
-    dw[i] = f32_to_bf16(s);
+    if (i >= n4) return;
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < splits; ++k) {
+        const float4 v = ws[(int64_t)k * n4 + i];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    dw[i] = uint2{f32x2_to_bf16x2(s.x, s.y), f32x2_to_bf16x2(s.z, s.w)};
 }
 
 }  // namespace convfwd

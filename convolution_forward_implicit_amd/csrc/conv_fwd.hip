@@ -111,6 +111,19 @@ void launch_wgrad(const WgradParams &wp, int grid, hipStream_t s)
     hipLaunchKernelGGL((wgrad_kernel<KT, KT, TT>), dim3(grid), dim3(256), 0, s, wp);
 }
 
+// Workgroups of one backward-weight instantiation that a compute unit holds
+// at once (its registers and LDS decide); 1 when the runtime cannot tell.
+template <int KT, int TT>
+int wgrad_occupancy()
+{
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, wgrad_kernel<KT, KT, TT>, 256, 0) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    return blocks > 0 ? blocks : 1;
+}
+
 enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2 };
 
 struct TileCfg {
@@ -327,6 +340,7 @@ struct conv_bwd_weight_plan {
     conv_fwd_desc_t desc;     // the forward problem
     WgradParams wp;           // pointers filled per run
     int KT, TT;               // tile: KT x KT channels, TT taps
+    int occ;                  // workgroups per CU at once
     int grid;
     int64_t x_elems, dy_elems, dw_elems, ws_bytes;
     char text[320];
@@ -1034,8 +1048,20 @@ conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weigh
     wp.tg_n = taps / pl->TT;
     const int64_t tiles = d.G * wp.kt_n * wp.ct_n * wp.tg_n;
     const int64_t steps = (wp.pixels + 31) / 32;
-    // split the pixels so that about two workgroups per compute unit run
-    int64_t splits = std::max<int64_t>(1, std::min<int64_t>(steps, (2 * device_cu_count() + tiles - 1) / tiles));
+    // Split the pixels so that all workgroups run in one round (as many as
+    // the CUs hold at once: one for the large tiles, several for the small
+    // ones) and each has at least 8 steps: every split writes a whole fp32
+    // partial tile that the reduction reads back, so more splits than the
+    // CUs can run at once only add traffic (at 112 splits of the grouped 2-D
+    // workload the reduction took a third of the time).
+    int occ = 1;
+    if (pl->KT == 64) occ = pl->TT == 9 ? wgrad_occupancy<64, 9>() : pl->TT == 3 ? wgrad_occupancy<64, 3>()
+                                                                                   : wgrad_occupancy<64, 1>();
+    else occ = pl->TT == 27 ? wgrad_occupancy<32, 27>() : pl->TT == 9 ? wgrad_occupancy<32, 9>()
+                            : pl->TT == 3 ? wgrad_occupancy<32, 3>() : wgrad_occupancy<32, 1>();
+    pl->occ = occ;
+    int64_t splits = std::max<int64_t>(1, (int64_t)device_cu_count() * occ / tiles);
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, steps / 8));
     const int64_t per = std::max<int64_t>(1, (steps + splits - 1) / splits);
     splits = std::max<int64_t>(1, (steps + per - 1) / per);
     wp.splits = (int)splits;
@@ -1051,8 +1077,9 @@ conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weigh
     pl->grid = (int)grid;
     pl->ws_bytes = pl->dw_elems * splits * 4;
     snprintf(pl->text, sizeof(pl->text),
-             "bwd_weight bf16 tile %dx%d ch x %d taps, %lld tiles x %d splits of %d x 32 pixels, grid=%d lds=%dB",
-             pl->KT, pl->KT, pl->TT, (long long)tiles, wp.splits, wp.steps_per_split, pl->grid,
+             "bwd_weight bf16 tile %dx%d ch x %d taps, %lld tiles x %d splits of %d x 32 pixels, grid=%d "
+             "(%d per CU) lds=%dB",
+             pl->KT, pl->KT, pl->TT, (long long)tiles, wp.splits, wp.steps_per_split, pl->grid, pl->occ,
              pl->KT == 64 ? (64 + pl->TT * 64) * 72 : (32 + pl->TT * 32) * 72);
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
@@ -1100,9 +1127,9 @@ conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void
         else if (plan->TT == 3) launch_wgrad<32, 3>(wp, plan->grid, s);
         else launch_wgrad<32, 1>(wp, plan->grid, s);
     }
-    const int64_t n = plan->dw_elems;
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       (const float *)workspace, (uint16_t *)dw, n, wp.splits);
+    const int64_t n = plan->dw_elems;   // a multiple of 8 (C % 8 == 0)
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                       (const float4 *)workspace, (uint2 *)dw, n / 4, wp.splits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return CONV_OK;
