@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) bwd_data_spread_kernel(SpreadParams sp)
 
 }  // namespace convfwd
 
-#include "igemm_kernel.h"
+#include "igemm_dma.h"
 
 namespace convfwd {
 
@@ -119,6 +119,7 @@ namespace convfwd {
 struct WgradParams {
     const void *x, *dy;
     float *ws;                 // partials [split][G][K][taps][C]
+    uint32_t x_bytes, dy_bytes;   // both below 2^31: 32-bit buffer offsets
     int N, G, C, K;
     int Di, Hi, Wi, Do, Ho, Wo;
     int sd, sh, sw, pd, ph, pw, dd, dh, dw;
@@ -129,7 +130,8 @@ struct WgradParams {
     FastDiv fd_Wo, fd_Ho, fd_Do;
 };
 
-typedef bf16x8_t bf16x8_a8 __attribute__((aligned(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
 template <int KT, int CT, int TT>
 struct WgradShape {
@@ -167,15 +169,21 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
     const int kti = b % wp.kt_n;
     const int g = b / wp.kt_n;
     const int k0 = kti * KT, c0 = cti * CT, t0 = tgi * TT;
-    const int64_t step0 = (int64_t)split * wp.steps_per_split;
-    const int64_t nsteps_total = (wp.pixels + S::PC - 1) / S::PC;
-    int64_t nsteps = nsteps_total - step0;
+    if (wp.pixels <= 0) return;
+    const int step0 = split * wp.steps_per_split;
+    const int nsteps_total = (int)((wp.pixels + S::PC - 1) / S::PC);
+    int nsteps = nsteps_total - step0;
     if (nsteps > wp.steps_per_split) nsteps = wp.steps_per_split;
+    const int pixels = (int)wp.pixels;
 
     // ---- this thread's staging units: row group r = tg + NTG*u, chunk q, pixel pair pp
-    const int q = tid % S::QN;
-    const int pp = (tid / S::QN) % (S::PC / 2);
-    const int tg = tid / (S::QN * S::PC / 2);
+    // pixel pairs fastest: the transposed LDS writes of a wave (rows 8q + e,
+    // dword column pp, 18-dword pitch) then fall at most two to a bank
+    const int pp = tid % (S::PC / 2);
+    const int q = (tid / (S::PC / 2)) % S::QN;
+    // a thread group spans whole waves (QN * PC / 2 is 64 or 128 threads)
+    const int tg = __builtin_amdgcn_readfirstlane(tid / (S::QN * S::PC / 2));
+    const int Di = wp.Di, Hi = wp.Hi, Wi = wp.Wi;
     int tz[S::UPT], ty[S::UPT], tx[S::UPT];     // tap offsets (row groups >= 1)
 #pragma unroll
     for (int u = 0; u < S::UPT; ++u) {
@@ -186,62 +194,94 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
         ty[u] = (yz % wp.Y) * wp.dh;
         tx[u] = xx * wp.dw;
     }
-    const uint16_t *xg = reinterpret_cast<const uint16_t *>(wp.x);
-    const uint16_t *dyg = reinterpret_cast<const uint16_t *>(wp.dy);
-    const int64_t GC = (int64_t)wp.G * wp.C, GK = (int64_t)wp.G * wp.K;
+    // Raw buffer loads with 32-bit byte offsets: an offset at or past the
+    // buffer's size (kOutOfRange) reads zeros, which is how padding, ragged
+    // channel tiles and pixels past the end are masked.
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(wp.x), (short)0,
+                                                                        (int)wp.x_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(wp.dy), (short)0,
+                                                                         (int)wp.dy_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r0 = tg == 0 ? rdy : rx;   // the first unit's tensor
+    // this thread's channel chunk of dy (k) and of x (c), as byte offsets
+    const int kq = k0 + 8 * q, cq = c0 + 8 * q;
+    const bool kin = kq < wp.K, cin = cq < wp.C;
+    const uint32_t dyq = (uint32_t)(g * wp.K + kq) * 2u, xq = (uint32_t)(g * wp.C + cq) * 2u;
+    const uint32_t gk2 = (uint32_t)(wp.G * wp.K) * 2u, gc2 = (uint32_t)(wp.G * wp.C) * 2u;
+    uint32_t toffb[S::UPT];                     // byte offset of each unit's tap
+#pragma unroll
+    for (int u = 0; u < S::UPT; ++u) toffb[u] = (uint32_t)((tz[u] * Hi + ty[u]) * Wi + tx[u]) * gc2;
 
-    uint4 v[S::UPT][2];
-    auto load = [&](int64_t step) {
+    // Staging registers, two steps deep.  Every unit issues its load, masked
+    // or not, so the loads of a step are a fixed count and the wait before a
+    // store covers the older step only.
+    u32x4_t v[2][S::UPT][2];
+    // The refill of one buffer in two parts: the pixel arithmetic of the
+    // thread's two pixels (prep), then one 16-byte load per (unit, pixel)
+    // (unit), so the loads can be spread between products.
+    struct Pix {
+        int id0, ih0, iw0;
+        uint32_t xb, dyoff;   // byte offset of tap (0, 0, 0) of the thread's chunk; dy's, or masked
+        bool pok;
+    };
+    Pix px[2];
+    auto prep = [&](int step) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int64_t P = step * S::PC + 2 * pp + h;
-            const bool pok = P < wp.pixels;
-            int n = 0, od = 0, oh = 0, ow = 0;
-            if (pok) {
-                const int pi = (int)P;
-                const int a = fdiv(pi, wp.fd_Wo);
-                ow = pi - a * wp.Wo;
-                const int b2 = fdiv(a, wp.fd_Ho);
-                oh = a - b2 * wp.Ho;
-                n = fdiv(b2, wp.fd_Do);
-                od = b2 - n * wp.Do;
-            }
-            const int id0 = od * wp.sd - wp.pd, ih0 = oh * wp.sh - wp.ph, iw0 = ow * wp.sw - wp.pw;
-#pragma unroll
-            for (int u = 0; u < S::UPT; ++u) {
-                const int r = tg + S::NTG * u;
-                uint4 val = {0u, 0u, 0u, 0u};
-                if (r < S::RG && pok) {
-                    if (r == 0) {
-                        const int k = k0 + 8 * q;
-                        if (k < wp.K) val = *reinterpret_cast<const uint4 *>(dyg + P * GK + (int64_t)g * wp.K + k);
-                    } else {
-                        const int c = c0 + 8 * q;
-                        const int id = id0 + tz[u], ih = ih0 + ty[u], iw = iw0 + tx[u];
-                        if (c < wp.C && (unsigned)id < (unsigned)wp.Di && (unsigned)ih < (unsigned)wp.Hi &&
-                            (unsigned)iw < (unsigned)wp.Wi)
-                            val = *reinterpret_cast<const uint4 *>(
-                                xg + ((((int64_t)n * wp.Di + id) * wp.Hi + ih) * wp.Wi + iw) * GC + (int64_t)g * wp.C + c);
-                    }
-                }
-                v[u][h] = val;
-            }
+            const int P = step * S::PC + 2 * pp + h;
+            const bool pok = P < pixels;
+            // a pixel past the end decomposes as the last one; its units are masked
+            const int pi = pok ? P : pixels - 1;
+            const int a = fdiv(pi, wp.fd_Wo);
+            const int ow = pi - a * wp.Wo;
+            const int b2 = fdiv(a, wp.fd_Ho);
+            const int oh = a - b2 * wp.Ho;
+            const int n = fdiv(b2, wp.fd_Do);
+            const int od = b2 - n * wp.Do;
+            Pix &x = px[h];
+            x.id0 = od * wp.sd - wp.pd;
+            x.ih0 = oh * wp.sh - wp.ph;
+            x.iw0 = ow * wp.sw - wp.pw;
+            // pixel of tap (0, 0, 0), possibly in the padding: in-range taps wrap back
+            x.xb = xq + (uint32_t)(((n * Di + x.id0) * Hi + x.ih0) * Wi + x.iw0) * gc2;
+            // bitwise ands throughout: short-circuit forms become branches around the loads
+            x.dyoff = (pok & kin) ? dyq + (uint32_t)P * gk2 : kOutOfRange;
+            x.pok = pok;
         }
     };
+    auto unit = [&](int bsel, int u, int h) __attribute__((always_inline)) {
+        const Pix &x = px[h];
+        const int r = tg + S::NTG * u;
+        // a unit past the last row group loads a masked offset too
+        const bool live = S::RG % S::NTG == 0 || r < S::RG;
+        const bool in = live & x.pok & cin & ((unsigned)(x.id0 + tz[u]) < (unsigned)Di) &
+                        ((unsigned)(x.ih0 + ty[u]) < (unsigned)Hi) & ((unsigned)(x.iw0 + tx[u]) < (unsigned)Wi);
+        const uint32_t xoff = in ? x.xb + toffb[u] : kOutOfRange;
+        // row group 0 is dy (thread group 0, first unit), the rest are taps of x
+        if (u == 0)
+            v[bsel][u][h] = __builtin_amdgcn_raw_buffer_load_b128(r0, tg == 0 ? x.dyoff : xoff, 0, 0);
+        else
+            v[bsel][u][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff, 0, 0);
+    };
+    auto load = [&](int bsel, int step) __attribute__((always_inline)) {
+        prep(step);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < S::UPT; ++u) unit(bsel, u, h);
+    };
     // transposed store: row (row group base + 8q + e), dword column pp = pixels (2pp, 2pp+1)
-    auto store = [&]() {
+    auto store = [&](int bsel) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < S::UPT; ++u) {
             const int r = tg + S::NTG * u;
             if (r < S::RG) {
                 const int row0 = (r == 0 ? 0 : KT + (r - 1) * CT) + 8 * q;
-                const uint32_t lo[4] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w};
-                const uint32_t hi[4] = {v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+                const u32x4_t lo = v[bsel][u][0], hi = v[bsel][u][1];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t a = (lo[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    const uint32_t bb = (hi[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                    *reinterpret_cast<uint32_t *>(smem + (row0 + e) * S::PITCH + 4 * pp) = a | (bb << 16);
+                    // channel e of pixel 2pp in the low half, of pixel 2pp+1 in the high half
+                    const uint32_t w = __builtin_amdgcn_perm(hi[e >> 1], lo[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+                    *reinterpret_cast<uint32_t *>(smem + (row0 + e) * S::PITCH + 4 * pp) = w;
                 }
             }
         }
@@ -254,29 +294,64 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
     const int frow = lane & 31, kh = lane >> 5;
 
-    if (nsteps > 0) load(step0);
-    for (int64_t it = 0; it < nsteps; ++it) {
+    // Fragments are read as 32-bit words and reinterpreted as bf16 at the
+    // product (as bf16 vectors the compiler repacks them element by element).
+    // Every wave runs NBW blocks: a block past the last (when 4 does not
+    // divide the count) reads the last block's rows and its sums are never
+    // stored, so no read or product is predicated.
+    constexpr int NM = 2 * S::NBW;              // products per wave and step
+    constexpr int NL = 2 * S::UPT;              // loads per thread and step
+    // One step: the staged registers of buffer bsel go to LDS; the step's
+    // fragments are read; then its products run with the refill of buffer
+    // bsel two steps ahead interleaved (the refill's address arithmetic is
+    // VALU work the matrix unit does not wait for: one wave per SIMD has
+    // no other wave to hide it behind).  The refill is unconditional (past
+    // the split's last step it reads pixels that are never stored, or
+    // masked ones), which keeps the number of loads in flight the same on
+    // every path, so each store waits for its own step's loads only.
+    auto step = [&](int bsel, int it) __attribute__((always_inline)) {
         __syncthreads();                      // the previous step's fragments are read
-        store();
+        store(bsel);
         __syncthreads();                      // this step is in LDS
-        if (it + 1 < nsteps) load(step0 + it + 1);   // in flight during the products
+        u32x4_t fa[2][S::NBW], fb[2][S::NBW];
 #pragma unroll
-        for (int s = 0; s < S::PC / 16; ++s) {
+        for (int s = 0; s < 2; ++s) {
             const int co = 32 * s + 16 * kh;  // byte offset of the lane's 8 pixels
 #pragma unroll
             for (int i = 0; i < S::NBW; ++i) {
-                const int blk = wave + 4 * i;
-                if (blk < S::NBLK) {
-                    const int cb = blk % S::CB, kb = (blk / S::CB) % S::KB, t = blk / (S::CB * S::KB);
-                    // rows are 8-byte aligned (72-byte pitch): two 8-byte LDS reads per fragment
-                    const bf16x8_t a = *reinterpret_cast<const bf16x8_a8 *>(smem + (kb * 32 + frow) * S::PITCH + co);
-                    const bf16x8_t bv = *reinterpret_cast<const bf16x8_a8 *>(
-                        smem + (KT + t * CT + cb * 32 + frow) * S::PITCH + co);
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, acc[i], 0, 0, 0);
-                }
+                // block wave + 4i: with 2x2 channel blocks the wave keeps its
+                // (kb, cb) and i is the tap; with one channel block the block is the tap
+                int t, kb, cb;
+                if (S::CB * S::KB == 4) { t = i; kb = wave >> 1; cb = wave & 1; }
+                else { t = min(wave + 4 * i, S::NBLK - 1); kb = 0; cb = 0; }
+                // rows are 8-byte aligned (72-byte pitch): two 8-byte LDS reads per fragment
+                fa[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (kb * 32 + frow) * S::PITCH + co);
+                fb[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (KT + t * CT + cb * 32 + frow) * S::PITCH + co);
             }
         }
+        prep(step0 + it + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        // products, each followed by one load of the refill
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int s = m / S::NBW, i = m % S::NBW;
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[s][i]),
+                                                             __builtin_bit_cast(bf16x8_t, fb[s][i]), acc[i], 0, 0, 0);
+            if (m < NL) unit(bsel, m % S::UPT, m / S::UPT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int m = NM; m < NL; ++m) unit(bsel, m % S::UPT, m / S::UPT);
+    };
+
+    load(0, step0);
+    load(1, step0 + 1);
+    int it = 0;
+    for (; it + 1 < nsteps; it += 2) {
+        step(0, it);
+        step(1, it + 1);
     }
+    if (it < nsteps) step(0, it);
 
     // ---- partial tile: lane holds dw[k = kb*32 + 8j + 4kh + e][c = cb*32 + frow] of tap t
     float *wsg = wp.ws + ((int64_t)split * wp.G + g) * (int64_t)wp.K * wp.taps * wp.C;
@@ -298,14 +373,23 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
 }
 
 // dw[i] = bf16(sum over splits s, in order, of ws[s][i]), four elements per
-// thread (n4 = elements / 4)
-__global__ void __launch_bounds__(256) wgrad_reduce_kernel(const float4 *__restrict__ ws, uint2 *__restrict__ dw,
-                                                           int64_t n4, int splits)
+// thread (n4 = elements / 4).  The partials are read eight splits at a time,
+// all eight loads issued before the adds, which keep the split order.
+__global__ void __launch_bounds__(64) wgrad_reduce_kernel(const float4 *__restrict__ ws, uint2 *__restrict__ dw,
+                                                          int64_t n4, int splits)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
     if (i >= n4) return;
     float4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < splits; ++k) {
+    int k = 0;
+    for (; k + 8 <= splits; k += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = ws[(int64_t)(k + j) * n4 + i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w; }
+    }
+    for (; k < splits; ++k) {
         const float4 v = ws[(int64_t)k * n4 + i];
         s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }

@@ -1070,7 +1070,9 @@ conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weigh
     pl->dy_elems = wp.pixels * d.G * d.K;
     pl->dw_elems = d.G * d.K * taps * d.C;
     const double grid = (double)tiles * splits;
-    if (grid >= 2147483647.0 || (double)pl->dw_elems * splits >= 2147483647.0 * 4) {
+    // x and dy are read through 32-bit byte offsets
+    if (grid >= 2147483647.0 || (double)pl->dw_elems * splits >= 2147483647.0 * 4 ||
+        pl->x_elems * 2 >= (int64_t(1) << 31) || pl->dy_elems * 2 >= (int64_t(1) << 31)) {
         delete pl;
         return fail(CONV_ERR_UNSUPPORTED, "backward-weight: problem too large");
     }
@@ -1114,10 +1116,16 @@ conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void
     WgradParams wp = plan->wp;
     wp.x = x;
     wp.dy = dy;
+    wp.x_bytes = (uint32_t)(plan->x_elems * 2);
+    wp.dy_bytes = (uint32_t)(plan->dy_elems * 2);
     wp.ws = reinterpret_cast<float *>(workspace);
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    if (plan->KT == 64) {
+    // No pixels (an empty batch): x and dy may be null, so the products are
+    // skipped and the reduction over zero splits writes dw = 0.
+    const bool empty = plan->dy_elems == 0;
+    if (empty) {
+    } else if (plan->KT == 64) {
         if (plan->TT == 9) launch_wgrad<64, 9>(wp, plan->grid, s);
         else if (plan->TT == 3) launch_wgrad<64, 3>(wp, plan->grid, s);
         else launch_wgrad<64, 1>(wp, plan->grid, s);
@@ -1128,8 +1136,8 @@ conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void
         else launch_wgrad<32, 1>(wp, plan->grid, s);
     }
     const int64_t n = plan->dw_elems;   // a multiple of 8 (C % 8 == 0)
-    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
-                       (const float4 *)workspace, (uint2 *)dw, n / 4, wp.splits);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + 63) / 64)), dim3(64), 0, s,
+                       (const float4 *)workspace, (uint2 *)dw, n / 4, empty ? 0 : wp.splits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return CONV_OK;
