@@ -103,9 +103,9 @@ namespace convfwd {
 // operands keep the channels innermost, so every K-step stages PC pixels of
 // dy (KT channels) and of x for each of TT taps (CT channels) in LDS
 // TRANSPOSED: one 72-byte row per channel holding its PC = 32 pixels (16-bit
-// values, pixel pairs in one dword; the 18-dword pitch keeps the 64 lanes of
-// a staging store in distinct bank pairs).  Loads are 16 bytes (8 channels of
-// one pixel) and coalesced along the channels.
+// values, pixel pairs in one dword; with the lanes running over pixel pairs
+// fastest, the 18-dword pitch puts at most two lanes of a staging store on a
+// bank).  Loads are 16 bytes (8 channels of one pixel).
 //
 // A workgroup owns a KT x CT block of (k, c) for TT taps of one group and a
 // contiguous range of pixel steps (split-K over the pixels: a weight
