@@ -454,6 +454,25 @@ def test_bwd_data_grouped_workloads_full_size_sampled(dev, wid):
     assert st["ok"], st
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+def test_bwd_data_frontend_full_size_sampled(dev, wid):
+    """Both layers of the fp32 batch-1 and bf16 batch-32 frontends at full
+    size, in the launch the benchmark's backward-data pass times: 4000
+    random input-gradient elements plus a stride through the tensor."""
+    W = sd.workload(wid)
+    dt = W["dtype"]
+    for li, (p, _, _) in enumerate(W["layers"]):
+        dy = _dy(p, dt, 110 + li, "float")
+        dx, _ = run_bwd_data(dev, p, dt, dy, W["w"][li])
+        n = int(np.prod(ref.shapes(p)[0]))
+        rng = np.random.Generator(np.random.PCG64(112 + li))
+        idx = np.unique(np.concatenate([rng.integers(0, n, 4000), np.arange(0, n, n // 97)]))
+        r, a = ref.conv_bwd_data_points(p, dy, W["w"][li], idx)
+        st = check.check(host(dx).ravel()[idx], r, a, _terms(p["K"] * np.prod(p["filt"])), dt, False, False)
+        print("parity:", li, {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+        assert st["ok"], (li, st)
+
+
 def test_bwd_data_empty_batch(dev):
     from convolution_forward_implicit_amd import ConvBwdData
     p = sd.conv1d_problem(0, 8, 8, 20, 3, 2, 1)
@@ -475,6 +494,10 @@ WGRAD = [
     ("wide_channels_k5", sd.conv1d_problem(1, 96, 80, 200, 5, 1, 2)),
     ("ragged_tiles", sd.problem(3, 1, 72, 40, (1, 7, 9), (1, 3, 3), (1, 1, 2), (0, 1, 1), (1, 1, 1))),
     ("pointwise", sd.problem(2, 2, 64, 64, (1, 6, 7), (1, 1, 1))),
+    # 32-channel tiles with 3 taps and with 1 tap: waves past the last block
+    # read a clamped block whose sums are never stored
+    ("kt32_taps3", sd.conv1d_problem(2, 32, 32, 150, 3, 1, 1)),
+    ("kt32_taps5_ragged", sd.conv1d_problem(3, 16, 24, 97, 5, 2, 2)),
 ]
 
 
@@ -525,6 +548,28 @@ def test_bwd_weight_grouped_workloads_full_size_sampled(dev, wid):
     st = check.check(host(dw).ravel()[idx], r, a, _terms(_pixels(p)), "bf16", False, False)
     print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
     assert st["ok"], st
+
+
+def test_bwd_weight_frontend_full_size_sampled(dev):
+    """Both layers of the bf16 batch-32 frontend at full size, in the launch
+    the benchmark's backward-weight pass times (layer 2's input a seeded
+    U[-1, 1) tensor of its shape): 2000 random weight-gradient elements, each
+    a sum over all 96000 or 48000 output pixels."""
+    W = sd.workload(3)
+    for li, (p, _, _) in enumerate(W["layers"]):
+        if li == 0:
+            x = W["x"]
+        else:
+            rng = np.random.Generator(np.random.PCG64(120))
+            x = sd.round_bf16(rng.uniform(-1.0, 1.0, size=ref.shapes(p)[0]).astype(np.float32))
+        dy = _dy(p, "bf16", 121 + li, "float")
+        dw, _ = run_bwd_weight(dev, p, x, dy)
+        n = int(np.prod(ref.shapes(p)[1]))
+        idx = np.unique(np.random.Generator(np.random.PCG64(123 + li)).integers(0, n, 2000))
+        r, a = ref.conv_bwd_weight_points(p, x, dy, idx)
+        st = check.check(host(dw).ravel()[idx], r, a, _terms(_pixels(p)), "bf16", False, False)
+        print("parity:", li, {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+        assert st["ok"], (li, st)
 
 
 def test_bwd_weight_empty_batch_is_zero_and_repeatable(dev):
