@@ -57,7 +57,7 @@ void launch_reg(const KParams &kp, uint32_t, uint32_t, int grid, hipStream_t s, 
 
 // The epilogue (bias, GELU) is compiled into each kernel variant, so a
 // variant carries only the code it runs.
-template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG>
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG, int FL>
 void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
                 hipEvent_t e1)
 {
@@ -68,13 +68,13 @@ void launch_dma(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream
     const dim3 g(grid), b(WM * WN * 64 * KG);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, true, true>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL, true, true>), g, b, 0, s, e0, e1, 0, dp);
     else if (bias)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, true, false>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL, true, false>), g, b, 0, s, e0, e1, 0, dp);
     else if (kp.gelu)
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, false, true>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL, false, true>), g, b, 0, s, e0, e1, 0, dp);
     else
-        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, false, false>), g, b, 0, s, e0, e1, 0, dp);
+        hipExtLaunchKernelGGL((igemm_dma_kernel<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL, false, false>), g, b, 0, s, e0, e1, 0, dp);
 }
 
 FastDiv make_fastdiv(int d);
@@ -149,16 +149,25 @@ struct TileCfg {
 #define DMA(DT, BM, BN, WM, WN, NS, MF, KSUB)                                            \
     TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
             DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, 1>::LDS_BYTES,                     \
-            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1>,                            \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1, 0>,                            \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB  \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB), \
+            0, 0, 0, 0, 0, 0, 1}
+
+// Loads of the next stage issued during the first 1/FL of the products
+#define DMAF(DT, BM, BN, WM, WN, NS, MF, KSUB, FL)                                       \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
+            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, 1>::LDS_BYTES,                     \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1, FL>,                        \
+            (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_f" #FL \
+                : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_f" #FL), \
             0, 0, 0, 0, 0, 0, 1}
 
 // Two reduction groups per workgroup (twice the waves, half the K-steps each)
 #define DMA2(DT, BM, BN, WM, WN, NS, MF, KSUB)                                           \
     TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
             DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, 2>::LDS_BYTES,                     \
-            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 2>,                            \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 2, 0>,                            \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2" \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2"), \
             0, 0, 0, 0, 0, 0, 2}
@@ -203,6 +212,8 @@ const TileCfg kCfgs[] = {
     DMA(1, 128, 32, 4, 1, 3, 16, 1),
     DMA(1, 64, 64, 2, 2, 3, 16, 1),
     DMA(1, 128, 128, 2, 2, 3, 32, 1),
+    DMAF(1, 192, 384, 2, 4, 2, 32, 1, 4),
+    DMAF(1, 256, 256, 2, 4, 2, 32, 1, 4),
     DMA(0, 32, 32, 2, 2, 2, 16, 1),
     DMA(0, 32, 32, 2, 2, 2, 16, 2),
     DMA(0, 32, 32, 2, 2, 2, 16, 4),

@@ -103,7 +103,14 @@ struct DmaShape {
     static constexpr int EPI = BM * LDC * ESZ;
     static constexpr int PART = (KG - 1) * BM * BN * 4;   // other group's fp32 partial tile
     static constexpr int PIPE = KG * NS * STAGE;
-    static constexpr int LDS_BYTES = PIPE > EPI ? (PIPE > PART ? PIPE : PART) : (EPI > PART ? EPI : PART);
+    static constexpr int BODY = PIPE > EPI ? (PIPE > PART ? PIPE : PART) : (EPI > PART ? EPI : PART);
+    // Big wave tiles (six or more MFMA blocks per wave) keep fewer operand
+    // registers live: fragments are read one 32-byte quarter of the slice
+    // at a time, the next quarter's while the current one is multiplied, and
+    // the bias sits in LDS (fp32, after the body) instead of registers.
+    static constexpr bool BIG = MI * NI >= 6;
+    static constexpr int BIAS_OFF = BODY;
+    static constexpr int LDS_BYTES = BIG ? BODY + BN * 4 : BODY;
 
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole DMA blocks per wave");
     static_assert(TM % MF == 0 && TN % MF == 0, "whole MFMA blocks per wave");
@@ -113,7 +120,12 @@ struct DmaShape {
     static_assert(KG == 1 || KG == 2, "one or two reduction groups");
 };
 
-template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG, bool BIAS, bool GELU>
+// FL = 0: the loads of the next stage are spread evenly over all products
+// of the current one; FL = f > 0: over the first 1/f of them, so that with
+// two stages the last load has most of a step to land before it is waited
+// for (spread evenly, the last one is issued just before that wait and its
+// whole latency is exposed on every step).
+template <int DT, int BM, int BN, int WM, int WN, int NS, int MF, int KSUB, int KG, int FL, bool BIAS, bool GELU>
 __global__ void __launch_bounds__(WM * WN * 64 * KG)
 igemm_dma_kernel(DmaParams dp)
 {
@@ -296,19 +308,67 @@ igemm_dma_kernel(DmaParams dp)
     constexpr int QS = (DT == 1 && MF == 32) ? 4 : 2;              // fragment reads per 128-byte row
     constexpr int EPQ = (DT == 1) ? 1 : 4;                         // products per fragment pair
     constexpr int NMF = KSUB * QS * EPQ * S::MI * S::NI;           // products per stage
-    auto compute = [&](int stage, int dst) {
+    constexpr int SPAN = FL > 0 ? (NMF + FL - 1) / FL : NMF;      // products the loads are spread over
+    typedef typename std::conditional<DT == 1, bf16x8_t, f32x4_t>::type Frag;
+    auto frag_off = [&](int q) {
+        const int ch = (MF == 32 && DT == 1) ? 2 * q + fk : 4 * q + fk;
+        return ((ch ^ (frow & 7) ^ (sw4 & (frow >> 4))) << 4);
+    };
+    auto compute_big = [&](int stage, int dst) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
             const unsigned char *As = smem + (kg * NS + stage) * S::STAGE + u * S::SUB;
             const unsigned char *Bs = As + BM * 128;
-            typedef typename std::conditional<DT == 1, bf16x8_t, f32x4_t>::type Frag;
+            Frag a[2][S::MI], b[2][S::NI];
+            auto rd = [&](int q) {
+                const int sw = frag_off(q);
+#pragma unroll
+                for (int i = 0; i < S::MI; ++i)
+                    a[q & 1][i] = *reinterpret_cast<const Frag *>(As + (wm * S::TM + i * MF + frow) * 128 + sw);
+#pragma unroll
+                for (int j = 0; j < S::NI; ++j)
+                    b[q & 1][j] = *reinterpret_cast<const Frag *>(Bs + (wn * S::TN + j * MF + frow) * 128 + sw);
+            };
+            rd(0);
+#pragma unroll
+            for (int q = 0; q < QS; ++q) {
+                if (q + 1 < QS) rd(q + 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int e = 0; e < EPQ; ++e)
+#pragma unroll
+                    for (int i = 0; i < S::MI; ++i)
+#pragma unroll
+                        for (int j = 0; j < S::NI; ++j) {
+                            if constexpr (DT == 1 && MF == 32)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[q & 1][j], a[q & 1][i], acc[i][j], 0, 0, 0);
+                            else if constexpr (DT == 1)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[q & 1][j], a[q & 1][i], acc[i][j], 0, 0, 0);
+                            else
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q & 1][j][e], a[q & 1][i][e], acc[i][j], 0, 0, 0);
+                            const int m = (((u * QS + q) * EPQ + e) * S::MI + i) * S::NI + j;
+                            const int q0 = m < SPAN ? m * S::L / SPAN : S::L;
+                            const int q1 = m < SPAN ? (m + 1) * S::L / SPAN : S::L;
+                            if (dst >= 0) {
+#pragma unroll
+                                for (int qq = q0; qq < q1; ++qq) fire(dst, qq);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+            }
+        }
+    };
+    auto compute_all = [&](int stage, int dst) {
+#pragma unroll
+        for (int u = 0; u < KSUB; ++u) {
+            const unsigned char *As = smem + (kg * NS + stage) * S::STAGE + u * S::SUB;
+            const unsigned char *Bs = As + BM * 128;
             Frag a[QS][S::MI], b[QS][S::NI];
 #pragma unroll
             for (int q = 0; q < QS; ++q) {
                 // 32x32 blocks: lane half fk takes chunk 2q+fk; 16x16 blocks:
                 // lane quarter fk takes chunk 4q+fk
-                const int ch = (MF == 32 && DT == 1) ? 2 * q + fk : 4 * q + fk;
-                const int sw = ((ch ^ (frow & 7) ^ (sw4 & (frow >> 4))) << 4);
+                const int sw = frag_off(q);
 #pragma unroll
                 for (int i = 0; i < S::MI; ++i)
                     a[q][i] = *reinterpret_cast<const Frag *>(As + (wm * S::TM + i * MF + frow) * 128 + sw);
@@ -334,7 +394,8 @@ igemm_dma_kernel(DmaParams dp)
                                 // quarter fk holds chunk 4q+fk, product e uses its element e
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(b[q][j][e], a[q][i][e], acc[i][j], 0, 0, 0);
                             const int m = (((u * QS + q) * EPQ + e) * S::MI + i) * S::NI + j;
-                            const int q0 = m * S::L / NMF, q1 = (m + 1) * S::L / NMF;
+                            const int q0 = m < SPAN ? m * S::L / SPAN : S::L;
+                            const int q1 = m < SPAN ? (m + 1) * S::L / SPAN : S::L;
                             if (dst >= 0) {
 #pragma unroll
                                 for (int qq = q0; qq < q1; ++qq) fire(dst, qq);
@@ -343,6 +404,21 @@ igemm_dma_kernel(DmaParams dp)
                         }
         }
     };
+
+    auto compute = [&](int stage, int dst) {
+        if constexpr (S::BIG) compute_big(stage, dst);
+        else compute_all(stage, dst);
+    };
+
+    // Big tiles: the bias of the tile's output channels goes to LDS (fp32)
+    // now; the first barrier of the loop orders it before the epilogue.
+    if constexpr (BIAS && S::BIG) {
+        float *bs = reinterpret_cast<float *>(smem + S::BIAS_OFF);
+        for (int i = tid; i < BN; i += S::NT) {
+            const int n = n0 + i;
+            bs[i] = n < p.K ? to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n]) : 0.f;
+        }
+    }
 
     // ---- pipeline: stage it+NS-1 is loaded while stage it is multiplied ---
     // (both groups run the same nkh steps, so every barrier sees all waves)
@@ -366,8 +442,8 @@ igemm_dma_kernel(DmaParams dp)
     __syncthreads();
     // Bias of the lane's output channels (see the epilogue for the layout),
     // loaded here so that the last step's products hide its latency.
-    float bias_v[S::NI][RUNS][4];
-    if constexpr (BIAS) {
+    float bias_v[S::BIG ? 1 : S::NI][RUNS][4];
+    if constexpr (BIAS && !S::BIG) {
 #pragma unroll
         for (int j = 0; j < S::NI; ++j)
 #pragma unroll
@@ -420,7 +496,11 @@ igemm_dma_kernel(DmaParams dp)
         for (int h = 0; h < RUNS; ++h) {
             const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS) {
+            if constexpr (BIAS && S::BIG) {
+                const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + nl * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = t4[e];
+            } else if constexpr (BIAS) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bv[e] = bias_v[j][h][e];
             }

@@ -6,6 +6,7 @@ rtol 1e-4 (fp32 outputs) or 8e-3 (bf16 outputs).  Integer-valued inputs in
 bit for bit (bf16 outputs against the one nearest-even rounding of the exact
 value)."""
 import itertools
+import re
 
 import numpy as np
 import pytest
@@ -152,6 +153,26 @@ def test_every_config_ragged(dev, cfg, name):
         assert np.array_equal(host(y), r)
     else:
         assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
+
+
+BIG = [(i, n) for i, n in CONFIGS if re.search(r"_dma_\d+x(256|384)_", n)]
+
+
+@pytest.mark.parametrize("cfg,name", BIG, ids=[n for _, n in BIG])
+def test_big_tiles_several_channel_tiles(dev, cfg, name):
+    """The wide-N tiles (bias staged in LDS, fragments read a quarter of
+    the slice at a time) on a 1-D problem spanning several output-channel
+    tiles and several row tiles, both ragged, with bias + GELU (float) and
+    bit-exact in integers."""
+    p = sd.conv1d_problem(3, 48, 900, 301, 3, 2, 1)
+    x, w, b = sd.random_inputs(p, "bf16", 41, True)
+    y, c = run(dev, p, "bf16", x, w, b, True, config=cfg)
+    assert name in c.describe()
+    assert_close(host(y), p, "bf16", x, w, b, True)
+    xi, wi, bi = sd.random_inputs(p, "bf16", 42, True, kind="int")
+    y, _ = run(dev, p, "bf16", xi, wi, bi, False, config=cfg)
+    r = ref.conv_fwd(p, xi, wi, bi, False, want_absdot=False)
+    assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
 
 
 @pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
