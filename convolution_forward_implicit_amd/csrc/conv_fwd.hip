@@ -172,6 +172,15 @@ struct TileCfg {
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2"), \
             0, 0, 0, 0, 0, 0, 2}
 
+// Four one-wave reduction groups per workgroup (a quarter of the K-steps each)
+#define DMA4(DT, BM, BN, NS, MF, KSUB)                                                   \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), 1, 1, 16 / (DT ? 2 : 4), NS,  \
+            DmaShape<DT, BM, BN, 1, 1, NS, MF, KSUB, 4>::LDS_BYTES,                       \
+            &launch_dma<DT, BM, BN, 1, 1, NS, MF, KSUB, 4, 0>,                           \
+            (DT ? "bf16_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4"        \
+                : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4"),       \
+            0, 0, 0, 0, 0, 0, 4}
+
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
 // filter taps per depth tap.
@@ -230,6 +239,9 @@ const TileCfg kCfgs[] = {
     DMA2(0, 32, 64, 1, 4, 2, 16, 1),
     DMA2(0, 64, 32, 4, 1, 2, 16, 1),
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
+    DMA4(0, 48, 48, 2, 16, 1),
+    DMA4(0, 32, 32, 2, 16, 1),
+    DMA4(1, 64, 64, 2, 16, 1),
     DMA2(1, 128, 64, 2, 2, 2, 32, 1),
     DMA2(1, 64, 64, 2, 2, 2, 16, 1),
     DMA2(1, 128, 32, 4, 1, 2, 16, 1),

@@ -101,7 +101,8 @@ struct DmaShape {
     static constexpr int STAGE = SUB * KSUB;
     static constexpr int LDC = BN + VEC;
     static constexpr int EPI = BM * LDC * ESZ;
-    static constexpr int PART = (KG - 1) * BM * BN * 4;   // other group's fp32 partial tile
+    static constexpr int LDF = BN + 4;                      // row stride (floats) of a partial tile
+    static constexpr int PART = KG > 1 ? KG * BM * LDF * 4 : 0;   // every group's fp32 partial tile
     static constexpr int PIPE = KG * NS * STAGE;
     static constexpr int BODY = PIPE > EPI ? (PIPE > PART ? PIPE : PART) : (EPI > PART ? EPI : PART);
     // Big wave tiles (six or more MFMA blocks per wave) keep fewer operand
@@ -109,15 +110,18 @@ struct DmaShape {
     // at a time, the next quarter's while the current one is multiplied, and
     // the bias sits in LDS (fp32, after the body) instead of registers.
     static constexpr bool BIG = MI * NI >= 6;
+    // the bias in LDS: big tiles, and split reductions (whose epilogue is
+    // shared by all waves)
+    static constexpr bool BIAS_LDS = BIG || KG > 1;
     static constexpr int BIAS_OFF = BODY;
-    static constexpr int LDS_BYTES = BIG ? BODY + BN * 4 : BODY;
+    static constexpr int LDS_BYTES = BIAS_LDS ? BODY + BN * 4 : BODY;
 
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole DMA blocks per wave");
     static_assert(TM % MF == 0 && TN % MF == 0, "whole MFMA blocks per wave");
     static_assert(MF == 16 || (MF == 32 && DT == 1), "32x32 blocks: bf16 only");
     static_assert(NS >= 2 && L * (NS - 2) < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
-    static_assert(KG == 1 || KG == 2, "one or two reduction groups");
+    static_assert(KG == 1 || KG == 2 || KG == 4, "one, two or four reduction groups");
 };
 
 // FL = 0: the loads of the next stage are spread evenly over all products
@@ -139,14 +143,17 @@ igemm_dma_kernel(DmaParams dp)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // With KG = 2 the workgroup is two groups of WM x WN waves that split the
+    // With KG > 1 the workgroup is KG groups of WM x WN waves that split the
     // reduction: group kg runs K-steps kg*nkh .. kg*nkh + nkh - 1 (steps past
-    // the end load zeros) through its own LDS stages, and group 1 hands its
-    // partial tile to group 0 through LDS at the end, which adds it (a fixed
-    // order, so the sum is deterministic).  Twice the waves per tile, half the
-    // serial K-steps each: it pays for problems with few output tiles and a
-    // long reduction (measured 10-15% on 7x7 and 14x14 maps with 256-512
-    // channels; no change on the frontend layers).
+    // the end load zeros) through its own LDS stages, and groups 1 .. KG-1
+    // hand their partial tiles to group 0 through LDS at the end, which adds
+    // them in group order (a fixed order, so the sum is deterministic).  KG
+    // times the waves per tile, 1/KG of the serial K-steps each: it pays for
+    // problems with few output tiles and a long reduction (KG = 2: measured
+    // 10-15% on 7x7 and 14x14 maps with 256-512 channels).  KG = 4 with one
+    // wave per group lets a small problem be cut into exactly one tile per
+    // compute unit (the batch-1 fp32 frontend's 1500 x 384 outputs are 256
+    // tiles of 48 x 48) with all four SIMDs busy on it.
     const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave_all / S::NW;
     const int wave = wave_all - kg * S::NW;   // wave within the group
@@ -227,17 +234,43 @@ igemm_dma_kernel(DmaParams dp)
     const int nkh = (nk + KG - 1) / KG;
     const int kstart = kg * nkh;
 
-    // filter tap of reduction index r = k0 + chunk*VEC, stepped by one
-    // 128-byte sub-slice (SUBK elements) per call of prep
-    int r = kstart * S::BK + chunk * S::VEC;
-    int c, xk, yk, zk;
-    {
-        const int tap = fdiv(r, p.fd_C);
-        c = r - tap * p.C;
+    // Filter-tap position of the reduction index r, stepped by one 128-byte
+    // sub-slice (SUBK elements) per call of prep, with the tap's element
+    // offset from the row base kept in bytes and advanced by precomputed
+    // deltas (no multiplication or division in the loop).  When C is a whole
+    // number of sub-slices (the 384- and 64-channel workloads) every lane of
+    // a sub-slice sits in the same tap: the position is then tracked once
+    // for the workgroup (`tu`, uniform, scalar registers) and the lane's
+    // chunk offset is part of its row bases; otherwise per lane (`tl`).
+    struct TapPos { int r, c, xk, yk, zd, yh, xw, offb; };
+    const bool uni = p.C % S::SUBK == 0;
+    const int dXb = (p.dw * GC - p.C) * S::ESZ;                       // x tap -> x tap + 1
+    const int dYb = (p.dh * p.Wi - p.X * p.dw) * GC * S::ESZ;         // (X, y) -> (0, y + 1)
+    const int dZb = (p.dd * p.Hi * p.Wi - p.Y * p.dh * p.Wi) * GC * S::ESZ;   // (0, Y, z) -> (0, 0, z + 1)
+    auto tap_at = [&](int r0) {
+        TapPos t;
+        const int tap = fdiv(r0, p.fd_C);
+        t.r = r0;
+        t.c = r0 - tap * p.C;
         const int t2 = fdiv(tap, p.fd_X);
-        xk = tap - t2 * p.X;
-        zk = fdiv(t2, p.fd_Y);
-        yk = t2 - zk * p.Y;
+        t.xk = tap - t2 * p.X;
+        const int zk = fdiv(t2, p.fd_Y);
+        t.yk = t2 - zk * p.Y;
+        t.zd = zk * p.dd;
+        t.yh = t.yk * p.dh;
+        t.xw = t.xk * p.dw;
+        t.offb = (((t.zd * p.Hi + t.yh) * p.Wi + t.xw) * GC + t.c) * S::ESZ;
+        return t;
+    };
+    TapPos tu = tap_at(kstart * S::BK);
+    TapPos tl = tap_at(kstart * S::BK + chunk * S::VEC);
+    // byte offset of each A row's base (with the pair swap, and with the
+    // lane's chunk when the tap position is the workgroup's)
+    int a_base[S::A_PER_W];
+#pragma unroll
+    for (int t = 0; t < S::A_PER_W; ++t) {
+        const int swap = sw4 & ((wave * S::A_PER_W + t) >> 1);
+        a_base[t] = (a_off[t] + (swap ? pair_delta : 0) + (uni ? chunk * S::VEC : 0)) * S::ESZ;
     }
 
     // DMA offsets of one stage, computed ahead (prep) and issued one at a
@@ -245,35 +278,47 @@ igemm_dma_kernel(DmaParams dp)
     // address arithmetic and issue run in the shadow of the matrix core.
     constexpr int LPS = S::A_PER_W + S::B_PER_W;   // loads per wave and sub-slice
     uint32_t dv[KSUB][LPS];
-    auto prep = [&](int k0) {
+    auto prep_with = [&](TapPos &ts, int k0) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
-            const bool rok = r < p.Kred;
-            const int zd = zk * p.dd, yh = yk * p.dh, xw = xk * p.dw;
-            const int toff = ((zd * p.Hi + yh) * p.Wi + xw) * GC + c;
+            const bool rok = ts.r < p.Kred;
 #pragma unroll
             for (int t = 0; t < S::A_PER_W; ++t) {
-                const bool ok = rok && (unsigned)(a_bd[t] + zd) < (unsigned)p.Di &&
-                                (unsigned)(a_bh[t] + yh) < (unsigned)p.Hi &&
-                                (unsigned)(a_bw[t] + xw) < (unsigned)p.Wi;
-                const int swap = sw4 & ((wave * S::A_PER_W + t) >> 1);
-                dv[u][t] = ok ? (uint32_t)((a_off[t] + toff + (swap ? pair_delta : 0)) * S::ESZ) : kOutOfRange;
+                const bool ok = rok && (unsigned)(a_bd[t] + ts.zd) < (unsigned)p.Di &&
+                                (unsigned)(a_bh[t] + ts.yh) < (unsigned)p.Hi &&
+                                (unsigned)(a_bw[t] + ts.xw) < (unsigned)p.Wi;
+                dv[u][t] = ok ? (uint32_t)(a_base[t] + ts.offb) : kOutOfRange;
             }
             const uint32_t kb = (uint32_t)((k0 + u * S::SUBK) * S::ESZ);
 #pragma unroll
             for (int t = 0; t < S::B_PER_W; ++t)
                 dv[u][S::A_PER_W + t] = (rok && b_off[t] != kOutOfRange) ? b_off[t] + kb : kOutOfRange;
             // advance to the next sub-slice
-            r += S::SUBK;
-            c += S::SUBK;
-            while (c >= p.C) {
-                c -= p.C;
-                if (++xk == p.X) {
-                    xk = 0;
-                    if (++yk == p.Y) { yk = 0; ++zk; }
+            ts.r += S::SUBK;
+            ts.c += S::SUBK;
+            ts.offb += S::SUBK * S::ESZ;
+            while (ts.c >= p.C) {
+                ts.c -= p.C;
+                ts.offb += dXb;
+                ts.xw += p.dw;
+                if (++ts.xk == p.X) {
+                    ts.xk = 0;
+                    ts.xw = 0;
+                    ts.offb += dYb;
+                    ts.yh += p.dh;
+                    if (++ts.yk == p.Y) {
+                        ts.yk = 0;
+                        ts.yh = 0;
+                        ts.offb += dZb;
+                        ts.zd += p.dd;
+                    }
                 }
             }
         }
+    };
+    auto prep = [&](int k0) {
+        if (uni) prep_with(tu, k0);
+        else prep_with(tl, k0);
     };
     // load number q (0 .. L-1) of the prepared stage into LDS stage `stage`
     auto fire = [&](int stage, int q) {
@@ -412,7 +457,7 @@ igemm_dma_kernel(DmaParams dp)
 
     // Big tiles: the bias of the tile's output channels goes to LDS (fp32)
     // now; the first barrier of the loop orders it before the epilogue.
-    if constexpr (BIAS && S::BIG) {
+    if constexpr (BIAS && S::BIAS_LDS) {
         float *bs = reinterpret_cast<float *>(smem + S::BIAS_OFF);
         for (int i = tid; i < BN; i += S::NT) {
             const int n = n0 + i;
@@ -442,8 +487,8 @@ igemm_dma_kernel(DmaParams dp)
     __syncthreads();
     // Bias of the lane's output channels (see the epilogue for the layout),
     // loaded here so that the last step's products hide its latency.
-    float bias_v[S::BIG ? 1 : S::NI][RUNS][4];
-    if constexpr (BIAS && !S::BIG) {
+    float bias_v[S::BIAS_LDS ? 1 : S::NI][RUNS][4];
+    if constexpr (BIAS && !S::BIAS_LDS) {
 #pragma unroll
         for (int j = 0; j < S::NI; ++j)
 #pragma unroll
@@ -459,29 +504,78 @@ igemm_dma_kernel(DmaParams dp)
     compute((nkh - 1) % NS, -1);
     __syncthreads();
 
-    // ---- group 1's partial tile into group 0's accumulators ---------------
-    if constexpr (KG == 2) {
-        float *part = reinterpret_cast<float *>(smem);   // [wave][i][j][e][lane]
-        if (kg == 1) {
+    T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;
+    const int GK = p.G * p.K;
+    constexpr int OVPR = BN / S::VEC;
+
+    // ---- split reduction: all waves share the epilogue ---------------------
+    // Every group's fp32 partial tile goes to LDS (row-major, rows of LDF
+    // floats); then each thread takes VEC consecutive outputs of a row, adds
+    // the KG partials in group order (a fixed order, so the result is
+    // deterministic), then bias, GELU, rounding, one 16-byte store.
+    if constexpr (KG > 1) {
+        float *pt = reinterpret_cast<float *>(smem);
+        float *mine = pt + kg * BM * S::LDF;
 #pragma unroll
-            for (int i = 0; i < S::MI; ++i)
+        for (int j = 0; j < S::NI; ++j)
 #pragma unroll
-                for (int j = 0; j < S::NI; ++j)
+            for (int h = 0; h < RUNS; ++h) {
+                const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
 #pragma unroll
-                    for (int e = 0; e < S::ACC; ++e)
-                        part[(((wave * S::MI + i) * S::NI + j) * S::ACC + e) * 64 + lane] = acc[i][j][e];
-        }
+                for (int i = 0; i < S::MI; ++i) {
+                    const int ml = wm * S::TM + i * MF + frow;
+                    *reinterpret_cast<f32x4_t *>(mine + ml * S::LDF + nl) =
+                        f32x4_t{acc[i][j][h * 4], acc[i][j][h * 4 + 1], acc[i][j][h * 4 + 2], acc[i][j][h * 4 + 3]};
+                }
+            }
         __syncthreads();
-        if (kg == 0) {
+        for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
+            const int row = idx / OVPR;
+            const int cv = idx % OVPR;
+            const int m = m0 + row;
+            const int n = n0 + cv * S::VEC;
+            if (m >= p.M || n >= p.K) continue;
+            float v[S::VEC];
 #pragma unroll
-            for (int i = 0; i < S::MI; ++i)
+            for (int q4 = 0; q4 < S::VEC / 4; ++q4) {
+                f32x4_t sum = *reinterpret_cast<const f32x4_t *>(pt + row * S::LDF + cv * S::VEC + q4 * 4);
 #pragma unroll
-                for (int j = 0; j < S::NI; ++j)
+                for (int g2 = 1; g2 < KG; ++g2)
+                    sum += *reinterpret_cast<const f32x4_t *>(pt + (g2 * BM + row) * S::LDF + cv * S::VEC + q4 * 4);
+                f32x4_t bv = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS)
+                    bv = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + (cv * S::VEC + q4 * 4) * 4);
 #pragma unroll
-                    for (int e = 0; e < S::ACC; ++e)
-                        acc[i][j][e] += part[(((wave * S::MI + i) * S::NI + j) * S::ACC + e) * 64 + lane];
+                for (int e = 0; e < 4; ++e) {
+                    float t = sum[e] + bv[e];
+                    if constexpr (GELU) t = gelu_erf(t);
+                    v[q4 * 4 + e] = t;
+                }
+            }
+            T *dst = yg + (size_t)m * GK + n;
+            if constexpr (DT == 1) {
+                uint4 pk;
+                pk.x = f32x2_to_bf16x2(v[0], v[1]);
+                pk.y = f32x2_to_bf16x2(v[2], v[3]);
+                pk.z = f32x2_to_bf16x2(v[4], v[5]);
+                pk.w = f32x2_to_bf16x2(v[6], v[7]);
+                if (p.out_vec) {
+                    *reinterpret_cast<uint4 *>(dst) = pk;
+                } else {
+                    const uint16_t *hv = reinterpret_cast<const uint16_t *>(&pk);
+                    const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
+                    for (int e = 0; e < lim; ++e) dst[e] = hv[e];
+                }
+            } else {
+                if (p.out_vec) {
+                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+                } else {
+                    const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
+                    for (int e = 0; e < lim; ++e) dst[e] = v[e];
+                }
+            }
         }
-        __syncthreads();                        // the staging below reuses the same bytes
+        return;
     }
 
     // ---- epilogue: bias, GELU, round, stage in LDS, whole-vector stores ---
@@ -496,7 +590,7 @@ igemm_dma_kernel(DmaParams dp)
         for (int h = 0; h < RUNS; ++h) {
             const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
             float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS && S::BIG) {
+            if constexpr (BIAS && S::BIAS_LDS) {
                 const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + nl * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) bv[e] = t4[e];
@@ -526,9 +620,6 @@ igemm_dma_kernel(DmaParams dp)
     }
     __syncthreads();
 
-    T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;
-    const int GK = p.G * p.K;
-    constexpr int OVPR = BN / S::VEC;
     for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
         const int row = idx / OVPR;
         const int cv = idx % OVPR;

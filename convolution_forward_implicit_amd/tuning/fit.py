@@ -36,10 +36,10 @@ def cfg_tile(name):
     m = re.match(r"bf16_patch_(\d+)x(\d+)x(\d+)_c(\d+)_s\d_p\d+x\d+_d\d$", name)
     if m:
         return ("patch",) + tuple(int(v) for v in m.groups())
-    m = re.match(r"(f32|bf16)_dma_(\d+)x(\d+)_w\dx\d_s\d_m\d+_k(\d)(_g2)?(_f\d)?$", name)
+    m = re.match(r"(f32|bf16)_dma_(\d+)x(\d+)_w\dx\d_s\d_m\d+_k(\d)(_g\d)?(_f\d)?$", name)
     if m:
         esz = 2 if m.group(1) == "bf16" else 4
-        return int(m.group(2)), int(m.group(3)), int(m.group(4)) * 128 // esz, 2 if m.group(5) else 1
+        return int(m.group(2)), int(m.group(3)), int(m.group(4)) * 128 // esz, int(m.group(5)[2:]) if m.group(5) else 1
     m = re.match(r"(f32|bf16)_(\d+)x(\d+)x(\d+)_w\dx\d_v\d$", name)
     return int(m.group(2)), int(m.group(3)), int(m.group(4)), 1
 

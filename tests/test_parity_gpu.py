@@ -175,6 +175,33 @@ def test_big_tiles_several_channel_tiles(dev, cfg, name):
     assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
 
 
+DMA_CONFIGS = [(i, n) for i, n in CONFIGS if "_dma_" in n]
+
+
+@pytest.mark.parametrize("cfg,name", DMA_CONFIGS, ids=[n for _, n in DMA_CONFIGS])
+def test_dma_configs_whole_subslice_channels(dev, cfg, name):
+    """Channel counts that are a whole number of 128-byte reduction
+    sub-slices (64 bf16 / 32 or 64 fp32): the direct-to-LDS kernel then
+    tracks the filter tap once per workgroup instead of per lane.  A 3-D
+    problem with depth/height/width strides, dilations and padding (every
+    tap-carry delta is used, padding taps read zeros), ragged against the
+    tile in rows and output channels, with bias + GELU in floats and
+    bit-exact in integers."""
+    dt = "bf16" if name.startswith("bf16") else "f32"
+    p = sd.problem(2, 2, 64, 40, (5, 9, 8), (3, 2, 3), (2, 1, 2), (2, 1, 3), (2, 3, 1))
+    x, w, b = sd.random_inputs(p, dt, 35, True)
+    y, c = run(dev, p, dt, x, w, b, True, config=cfg)
+    assert name in c.describe()
+    assert_close(host(y), p, dt, x, w, b, True)
+    xi, wi, bi = sd.random_inputs(p, dt, 36, True, kind="int")
+    y, _ = run(dev, p, dt, xi, wi, bi, False, config=cfg)
+    r = ref.conv_fwd(p, xi, wi, bi, False, want_absdot=False)
+    if dt == "f32":
+        assert np.array_equal(host(y), r)
+    else:
+        assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
+
+
 @pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
 def test_every_config_3d_strided_dilated(dev, cfg, name):
     dt = "bf16" if name.startswith("bf16") else "f32"
