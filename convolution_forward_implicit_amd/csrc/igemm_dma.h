@@ -58,10 +58,28 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes)
     return r;
 }
 
+// The buffer descriptor, the scalar offset and the LDS address of a load
+// are the same in every lane.  Where the compiler cannot prove that (values
+// that pass through code with divergent branches), it keeps them in vector
+// registers, which the instruction cannot take: take them from the first
+// active lane.
+__device__ __forceinline__ i32x4_t uniform_rsrc(i32x4_t r)
+{
+    i32x4_t o;
+    o[0] = __builtin_amdgcn_readfirstlane(r[0]);
+    o[1] = __builtin_amdgcn_readfirstlane(r[1]);
+    o[2] = __builtin_amdgcn_readfirstlane(r[2]);
+    o[3] = __builtin_amdgcn_readfirstlane(r[3]);
+    return o;
+}
+
 // One 16-byte-per-lane load into LDS at lds_addr + 16 * lane.  M0 carries
 // the LDS address and is restored afterwards.
 __device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds_addr)
 {
+    rsrc = uniform_rsrc(rsrc);
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
@@ -242,12 +260,14 @@ igemm_dma_kernel(DmaParams dp)
     // a sub-slice sits in the same tap: the position is then tracked once
     // for the workgroup (`tu`, uniform, scalar registers) and the lane's
     // chunk offset is part of its row bases; otherwise per lane (`tl`).
+    // (Every helper lambda here is forced inline: one left as a call passes
+    // its by-reference captures through scratch memory.)
     struct TapPos { int r, c, xk, yk, zd, yh, xw, offb; };
     const bool uni = p.C % S::SUBK == 0;
     const int dXb = (p.dw * GC - p.C) * S::ESZ;                       // x tap -> x tap + 1
     const int dYb = (p.dh * p.Wi - p.X * p.dw) * GC * S::ESZ;         // (X, y) -> (0, y + 1)
     const int dZb = (p.dd * p.Hi * p.Wi - p.Y * p.dh * p.Wi) * GC * S::ESZ;   // (0, Y, z) -> (0, 0, z + 1)
-    auto tap_at = [&](int r0) {
+    auto tap_at = [&](int r0) __attribute__((always_inline)) {
         TapPos t;
         const int tap = fdiv(r0, p.fd_C);
         t.r = r0;
@@ -278,7 +298,7 @@ igemm_dma_kernel(DmaParams dp)
     // address arithmetic and issue run in the shadow of the matrix core.
     constexpr int LPS = S::A_PER_W + S::B_PER_W;   // loads per wave and sub-slice
     uint32_t dv[KSUB][LPS];
-    auto prep_with = [&](TapPos &ts, int k0) {
+    auto prep_with = [&](TapPos &ts, int k0) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
             const bool rok = ts.r < p.Kred;
@@ -316,12 +336,12 @@ igemm_dma_kernel(DmaParams dp)
             }
         }
     };
-    auto prep = [&](int k0) {
+    auto prep = [&](int k0) __attribute__((always_inline)) {
         if (uni) prep_with(tu, k0);
         else prep_with(tl, k0);
     };
     // load number q (0 .. L-1) of the prepared stage into LDS stage `stage`
-    auto fire = [&](int stage, int q) {
+    auto fire = [&](int stage, int q) __attribute__((always_inline)) {
         const int u = q / LPS, t = q % LPS;
         const uint32_t base = lds0 + (kg * NS + stage) * S::STAGE + u * S::SUB;
         if (t < S::A_PER_W)
@@ -355,17 +375,17 @@ igemm_dma_kernel(DmaParams dp)
     constexpr int NMF = KSUB * QS * EPQ * S::MI * S::NI;           // products per stage
     constexpr int SPAN = FL > 0 ? (NMF + FL - 1) / FL : NMF;      // products the loads are spread over
     typedef typename std::conditional<DT == 1, bf16x8_t, f32x4_t>::type Frag;
-    auto frag_off = [&](int q) {
+    auto frag_off = [&](int q) __attribute__((always_inline)) {
         const int ch = (MF == 32 && DT == 1) ? 2 * q + fk : 4 * q + fk;
         return ((ch ^ (frow & 7) ^ (sw4 & (frow >> 4))) << 4);
     };
-    auto compute_big = [&](int stage, int dst) {
+    auto compute_big = [&](int stage, int dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
             const unsigned char *As = smem + (kg * NS + stage) * S::STAGE + u * S::SUB;
             const unsigned char *Bs = As + BM * 128;
             Frag a[2][S::MI], b[2][S::NI];
-            auto rd = [&](int q) {
+            auto rd = [&](int q) __attribute__((always_inline)) {
                 const int sw = frag_off(q);
 #pragma unroll
                 for (int i = 0; i < S::MI; ++i)
@@ -403,7 +423,7 @@ igemm_dma_kernel(DmaParams dp)
             }
         }
     };
-    auto compute_all = [&](int stage, int dst) {
+    auto compute_all = [&](int stage, int dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < KSUB; ++u) {
             const unsigned char *As = smem + (kg * NS + stage) * S::STAGE + u * S::SUB;
@@ -450,20 +470,10 @@ igemm_dma_kernel(DmaParams dp)
         }
     };
 
-    auto compute = [&](int stage, int dst) {
+    auto compute = [&](int stage, int dst) __attribute__((always_inline)) {
         if constexpr (S::BIG) compute_big(stage, dst);
         else compute_all(stage, dst);
     };
-
-    // Big tiles: the bias of the tile's output channels goes to LDS (fp32)
-    // now; the first barrier of the loop orders it before the epilogue.
-    if constexpr (BIAS && S::BIAS_LDS) {
-        float *bs = reinterpret_cast<float *>(smem + S::BIAS_OFF);
-        for (int i = tid; i < BN; i += S::NT) {
-            const int n = n0 + i;
-            bs[i] = n < p.K ? to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n]) : 0.f;
-        }
-    }
 
     // ---- pipeline: stage it+NS-1 is loaded while stage it is multiplied ---
     // (both groups run the same nkh steps, so every barrier sees all waves)
@@ -474,6 +484,18 @@ igemm_dma_kernel(DmaParams dp)
 #pragma unroll
             for (int q = 0; q < S::L; ++q) fire(s, q);
         }
+
+    // Big tiles and split reductions: the bias of the tile's output channels
+    // goes to LDS (fp32) once the first loads are in flight; the first
+    // barrier of the loop orders it before the epilogue.
+    if constexpr (BIAS && S::BIAS_LDS) {
+        float *bs = reinterpret_cast<float *>(smem + S::BIAS_OFF);
+        for (int i = tid; i < BN; i += S::NT) {
+            const int n = n0 + i;
+            bs[i] = n < p.K ? to_f32<T>(reinterpret_cast<const T *>(p.bias)[g * p.K + n]) : 0.f;
+        }
+    }
+
     for (int it = 0; it < nkh - 1; ++it) {
         if (it + NS - 2 < nkh) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
