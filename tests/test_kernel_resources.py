@@ -1,0 +1,60 @@
+"""CPU build checks of the direct-to-LDS implicit-GEMM kernel (no GPU):
+representative instantiations of every code path (wide-N tiles, four and
+two reduction groups, front-loaded loads, 16x16 and 32x32 bf16 blocks,
+fp32 blocks over two sub-slices; with and without the bias + GELU
+epilogue) are compiled for gfx950 and must use no scratch memory.  A helper
+lambda that the compiler leaves as a call passes its captures through
+scratch, which made such kernels 10-100x slower; register spills show up
+the same way."""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "convolution_forward_implicit_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# <DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL>
+INSTANCES = [
+    "1, 192, 384, 2, 4, 2, 32, 1, 1, 4",
+    "1, 256, 256, 2, 4, 2, 32, 1, 1, 4",
+    "0, 48, 48, 1, 1, 2, 16, 1, 4, 0",
+    "0, 32, 32, 2, 2, 2, 16, 2, 2, 0",
+    "0, 32, 32, 2, 2, 2, 16, 2, 1, 0",
+    "0, 32, 64, 1, 4, 2, 16, 2, 1, 0",
+    "1, 256, 64, 4, 1, 2, 32, 1, 1, 0",
+    "1, 128, 64, 2, 2, 2, 16, 1, 1, 0",
+    "1, 128, 128, 2, 2, 3, 32, 1, 1, 0",
+]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_dma_kernels_use_no_scratch():
+    lines = ['#include "igemm_dma.h"', "namespace convfwd {"]
+    for inst in INSTANCES:
+        for ep in ("true, true", "false, false"):
+            lines.append("template __global__ void igemm_dma_kernel<%s, %s>(DmaParams);" % (inst, ep))
+    lines.append("}")
+    d = tempfile.mkdtemp()
+    try:
+        src = os.path.join(d, "inst.hip")
+        with open(src, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-c", "--cuda-device-only",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I" + CSRC, "-I" + os.path.join(ROOT, "include"),
+               "-Rpass-analysis=kernel-resource-usage", src, "-o", os.path.join(d, "inst.o")]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=600)
+        assert r.returncode == 0, r.stdout[-3000:]
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    names = re.findall(r"Function Name: (\S+)", r.stdout)
+    scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stdout)]
+    spills = [int(v) for v in re.findall(r"VGPRs Spill: (\d+)", r.stdout)]
+    assert len(names) == 2 * len(INSTANCES) == len(scratch) == len(spills), r.stdout[-2000:]
+    bad = [(n, s, v) for n, s, v in zip(names, scratch, spills) if s or v]
+    assert not bad, bad
