@@ -240,6 +240,7 @@ const TileCfg kCfgs[] = {
     DMA2(0, 64, 32, 4, 1, 2, 16, 1),
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
     DMA4(0, 48, 48, 2, 16, 1),
+    DMA2(0, 48, 96, 1, 2, 2, 16, 2),
     DMA4(0, 32, 32, 2, 16, 1),
     DMA2(1, 128, 64, 2, 2, 2, 32, 1),
     DMA2(1, 64, 64, 2, 2, 2, 16, 1),
