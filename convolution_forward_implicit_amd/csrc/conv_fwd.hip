@@ -419,13 +419,15 @@ conv_status_t validate(const conv_fwd_desc_t *d, int64_t out[3])
     }
     if (d->G > (1 << 30) || d->C > (1 << 30) || d->K > (1 << 30) || d->N > (1 << 30))
         return fail(CONV_ERR_UNSUPPORTED, "N, G, C or K above 2^30");
-    // Every element offset the kernel forms, including the padding halo, must
-    // fit in a signed 32-bit integer.
+    // Every element offset the kernels form must fit in a signed 32-bit
+    // integer.  A row base or a tap offset stays within the zero-padded input
+    // (a coordinate lies in [-p, I + p): the last window ends inside the
+    // padding), so N x prod(I + 2p) x G x C bounds them all; a sum of the
+    // two is only formed for a tap inside the input.
     const double lim = 2147483647.0;
     const double gc = (double)d->G * (double)d->C, gk = (double)d->G * (double)d->K;
-    const double xpad = (double)std::max<int64_t>(d->N, 1) * (d->in[0] + 2.0 * d->pad[0] + d->stride[0] * 2.0 + d->dilation[0] * d->filt[0]) *
-                        (d->in[1] + 2.0 * d->pad[1] + d->stride[1] * 2.0 + d->dilation[1] * d->filt[1]) *
-                        (d->in[2] + 2.0 * d->pad[2] + d->stride[2] * 2.0 + d->dilation[2] * d->filt[2]) * gc;
+    const double xpad = (double)std::max<int64_t>(d->N, 1) * (d->in[0] + 2.0 * d->pad[0]) *
+                        (d->in[1] + 2.0 * d->pad[1]) * (d->in[2] + 2.0 * d->pad[2]) * gc;
     const double welem = gk * d->C * (double)d->filt[0] * d->filt[1] * d->filt[2];
     const double yelem = (double)d->N * out[0] * out[1] * out[2] * gk;
     if (xpad >= lim || welem >= lim || yelem >= lim)

@@ -136,3 +136,10 @@ def random_inputs(p, dtype, seed, has_bias, kind="float"):
     w = _store(rng.normal(0.0, 1.0 / np.sqrt(p["C"] * Z * Y * X), size=ws), dtype)
     b = _store(rng.normal(0.0, 0.02, size=bs), dtype) if has_bias else None
     return x, w, b
+
+
+def random_int8(shape, seed):
+    """Integers in {-2..2} as int8 (one byte per element, for inputs of
+    several GiB; exact in bf16 and fp32 once converted)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(-2, 3, size=shape, dtype=np.int8)

@@ -101,6 +101,25 @@ def test_create_rejects_invalid(kw, status):
     assert capi.conv_fwd_last_error()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_largest_inputs_32bit_offset_bound(dtype):
+    """The plan accepts an input whose zero-padded element count is just
+    below 2^31 (a 1-D conv with 1.07e9 input elements: 2 GiB in bf16, so
+    the 32-bit-byte-offset kernels are not eligible and the description
+    names a register-staged configuration) and rejects one just above."""
+    p = sd.conv1d_problem(16, 64, 16, 1048600, 3, 1, 1)
+    plan = capi.conv_fwd_create(desc_from_problem(p, dtype, True, False))
+    try:
+        text = capi.conv_fwd_describe(plan)
+        assert "_dma_" not in text and "_patch_" not in text
+    finally:
+        capi.conv_fwd_destroy(plan)
+    big = sd.conv1d_problem(32, 64, 16, 1048576, 3, 1, 1)   # 32 x 1048578 x 64 > 2^31 - 1
+    with pytest.raises(ConvError) as e:
+        capi.conv_fwd_create(desc_from_problem(big, dtype))
+    assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+
+
 def test_flags_must_be_boolean():
     d = desc_from_problem(sd.conv1d_problem(1, 4, 4, 8, 3, 1, 1), "f32")
     d.has_bias = 2

@@ -270,6 +270,31 @@ def test_edge_cases(dev, name, p, dt):
         assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
 
 
+def test_input_of_2gib_and_more_bit_exact(dev):
+    """An input of 2 GiB or more (bf16 [16, 1048600, 64], 2.00005 GiB): the
+    direct-to-LDS kernels address x with 32-bit byte offsets and are not
+    eligible, so the plan takes the register-staged kernel, whose 64-bit
+    addressing must reach the end of x.  Integer inputs, bit-exact on
+    sampled outputs that include the last images (x offsets past 2^31
+    bytes)."""
+    from convolution_forward_implicit_amd import ConvFwd
+    p = sd.conv1d_problem(16, 64, 16, 1048600, 3, 1, 1)
+    xs, ws, bs, ys = ref.shapes(p)
+    assert int(np.prod(xs)) * 2 >= 2 ** 31
+    x8, w8, b8 = sd.random_int8(xs, 71), sd.random_int8(ws, 72), sd.random_int8(bs, 73)
+    c = ConvFwd(p, "bf16", True, False)
+    print("case: 2 GiB input", p, c.describe(), flush=True)
+    assert "_dma_" not in c.describe() and "_patch_" not in c.describe()
+    t = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+    y = c(t(x8), t(w8), t(b8))
+    torch.cuda.synchronize()
+    idx = sample_indices(p, 3000, 74)
+    got = y.view(torch.int16).reshape(-1)[torch.from_numpy(idx).to(dev)].cpu().numpy().view(np.uint16)
+    del y
+    r = ref.conv_fwd_points(p, x8, w8, b8, False, idx)[0]
+    assert np.array_equal(got, check.round_to_bf16_bits(r))
+
+
 def test_empty_batch_leaves_output_untouched(dev):
     from convolution_forward_implicit_amd import ConvFwd
     p = sd.conv1d_problem(0, 8, 8, 16, 3, 1, 1)
