@@ -18,8 +18,12 @@ itself records when the kernel starts and ends (on the stream it runs on),
 against the MI355X dense MFMA peak of its dtype.  Those events are taken on
 every --event-every'th step of the timed region (default 8): a launch that
 records them costs the host ~10 us more, which at every step would show up
-in the step time of the small workloads.  cpu_baseline = the fp64
-oracle on the host cores over a bounded sample of the same workload.
+in the step time of the small workloads.  The warm-cache figures (value,
+roofline) run every step on one buffer set; cold = the same measurement
+rotating through device copies of the inputs, weights and outputs that
+total at least 512 MiB (twice the MALL), so no step finds its data in the
+L2 or the MALL.  cpu_baseline = the fp64 oracle on the host cores over a
+bounded sample of the same workload.
 
     python bench.py --copy-bytes B [--steps K]
 
@@ -39,6 +43,7 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense MFMA
 HBM_GBS = 8000.0
+COLD_POOL_BYTES = 512 << 20   # rotated buffer sets: twice the 256 MB MALL
 METRIC = "conv fwd useful TFLOP/s and % of MFMA peak (Whisper frontend, grouped bf16)"
 DEFAULT_WORKLOAD = "whisper_frontend_f32_b1"
 
@@ -124,6 +129,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--event-every", type=int, default=8,
                     help="record the dominant kernel's start/stop events on every N-th timed step")
+    ap.add_argument("--cold-steps", type=int, default=64,
+                    help="steps of the cold-cache measurement (rotating buffer sets); 0 skips it")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--fused", action="store_true",
@@ -166,8 +173,6 @@ def main():
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(tdt).contiguous()
 
-    convs, ws, bs, outs = [], [], [], []
-    x0 = up(W["x"])
     stream = torch.cuda.current_stream(dev)
     esz = 4 if dt == "f32" else 2
     fused = args.fused or args.fused_natural
@@ -177,15 +182,23 @@ def main():
             print("bench.py: --fused is a forward path", file=sys.stderr)
             sys.exit(2)
         return bench_backward(args, W, dt, tdt, dev, up)
+
+    # Buffer sets: set 0 holds the workload's seeded arrays; further sets are
+    # device copies of them, used by the cold-cache measurement, which
+    # rotates through enough sets that no step finds its inputs, weights or
+    # outputs in the L2 or the 256 MB MALL.
+    def clone(t):
+        return None if t is None else t.clone()
+
     if fused:
         if len(W["layers"]) != 2:
             print("bench.py: --fused needs a two-conv workload", file=sys.stderr)
             sys.exit(2)
         (p1, hb, ge), (p2, _, _) = W["layers"]
         chain = ConvChain(p1, p2, dt, hb, ge)
-        w1, w2 = up(W["w"][0]), up(W["w"][1])
-        b1, b2 = (up(W["b"][0]), up(W["b"][1])) if hb else (None, None)
-        y = torch.empty(chain.y_shape, dtype=tdt, device=dev)
+        base = {"x": up(W["x"]), "w1": up(W["w"][0]), "w2": up(W["w"][1]),
+                "b1": up(W["b"][0]) if hb else None, "b2": up(W["b"][1]) if hb else None,
+                "y": torch.empty(chain.y_shape, dtype=tdt, device=dev)}
         convs = [chain]
         flops = [chain.useful_flop()]
         dom = 0
@@ -193,72 +206,94 @@ def main():
                                int(np.prod(chain.w2_shape)) + (2 * int(np.prod(chain.b_shape)) if hb else 0) +
                                int(np.prod(chain.y_shape)))
 
-        if args.fused:
-            # weights are constant across steps: prepack once, as a model load would
-            wp = chain.pack(w1, w2, stream=stream)
-            pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            torch.cuda.synchronize()
-            pe[0].record(stream)
-            chain.pack(w1, w2, out=wp, stream=stream)
-            pe[1].record(stream)
-            torch.cuda.synchronize()
-            prepack = {"ms": round(pe[0].elapsed_time(pe[1]), 5), "bytes": int(wp.numel()),
-                       "when": "once, before the timed steps (weights are constant)"}
+        def make_set(first):
+            st = base if first else {k: clone(v) for k, v in base.items()}
+            if args.fused:
+                # weights are constant across steps: prepack once per set, as a model load would
+                st["wp"] = chain.pack(st["w1"], st["w2"], stream=stream)
+            return st
 
-            def step(ev=None, i=0):
-                kev = (ev[0][i], ev[1][i]) if ev is not None else None
-                chain.run_packed(x0, wp, b1, b2, out=y, stream=stream, events=kev)
-        else:
-            def step(ev=None, i=0):
-                kev = (ev[0][i], ev[1][i]) if ev is not None else None
-                chain(x0, w1, b1, w2, b2, out=y, stream=stream, events=kev)
+        def step(st, kev=None):
+            if args.fused:
+                chain.run_packed(st["x"], st["wp"], st["b1"], st["b2"], out=st["y"], stream=stream, events=kev)
+            else:
+                chain(st["x"], st["w1"], st["b1"], st["w2"], st["b2"], out=st["y"], stream=stream, events=kev)
     else:
-        for li, (p, hb, ge) in enumerate(W["layers"]):
-            c = ConvFwd(p, dt, hb, ge)
-            convs.append(c)
-            ws.append(up(W["w"][li]))
-            bs.append(up(W["b"][li]) if hb else None)
-            outs.append(torch.empty(c.y_shape, dtype=tdt, device=dev))
+        convs = [ConvFwd(p, dt, hb, ge) for p, hb, ge in W["layers"]]
+        base = {"x": up(W["x"]), "w": [up(w) for w in W["w"]],
+                "b": [up(b) if hb else None for b, (_, hb, _) in zip(W["b"], W["layers"])],
+                "outs": [torch.empty(c.y_shape, dtype=tdt, device=dev) for c in convs]}
         flops = [c.useful_flop() for c in convs]
         dom = int(np.argmax(flops))
         dom_alg_bytes = esz * (int(np.prod(convs[dom].x_shape)) + int(np.prod(convs[dom].w_shape)) +
                                (int(np.prod(convs[dom].b_shape)) if convs[dom].has_bias else 0) +
                                int(np.prod(convs[dom].y_shape)))
 
-        def step(ev=None, i=0):
-            x = x0
+        def make_set(first):
+            if first:
+                return base
+            return {"x": clone(base["x"]), "w": [clone(w) for w in base["w"]], "b": [clone(b) for b in base["b"]],
+                    "outs": [torch.empty_like(o) for o in base["outs"]]}
+
+        def step(st, kev=None):
+            x = st["x"]
             for li, c in enumerate(convs):
-                kev = (ev[0][i], ev[1][i]) if ev is not None and li == dom else None
-                c(x, ws[li], bs[li], out=outs[li], stream=stream, events=kev)
-                x = outs[li]
+                c(x, st["w"][li], st["b"][li], out=st["outs"][li], stream=stream, events=kev if li == dom else None)
+                x = st["outs"][li]
+
+    def set_bytes(st):
+        tot = 0
+        for v in st.values():
+            for t in (v if isinstance(v, list) else [v]):
+                if t is not None:
+                    tot += t.numel() * t.element_size()
+        return tot
+
+    sets = [make_set(True)]
+    if args.fused:
+        wp0 = sets[0]["wp"]
+        pe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.cuda.synchronize()
+        pe[0].record(stream)
+        chain.pack(sets[0]["w1"], sets[0]["w2"], out=wp0, stream=stream)
+        pe[1].record(stream)
+        torch.cuda.synchronize()
+        prepack = {"ms": round(pe[0].elapsed_time(pe[1]), 5), "bytes": int(wp0.numel()),
+                   "when": "once, before the timed steps (weights are constant)"}
+
+    def timed(K, E, pick):
+        """K steps (step i on buffer set pick(i)) between two device
+        synchronisations; the dominant kernel records start/stop events on
+        every E-th step.  Returns (ms per step, mean dominant-kernel ms,
+        launches timed, wall seconds)."""
+        NE = (K + E - 1) // E
+        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(NE)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(NE)])
+        for e in ev[0] + ev[1]:
+            e.record(stream)              # creates the event handles the kernel launch records
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(K):
+            st = sets[pick(i)]
+            if i % E == 0:
+                step(st, (ev[0][i // E], ev[1][i // E]))
+            else:
+                step(st)
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return (start.elapsed_time(end) / K, float(np.mean([a.elapsed_time(b) for a, b in zip(*ev)])), NE, wall)
 
     for _ in range(args.warmup):
-        step()
+        step(sets[0])
     torch.cuda.synchronize()
 
     K = args.steps
     E = max(1, args.event_every)
-    NE = (K + E - 1) // E             # steps whose dominant launch records events
-    ev = ([torch.cuda.Event(enable_timing=True) for _ in range(NE)],
-          [torch.cuda.Event(enable_timing=True) for _ in range(NE)])
-    for e in ev[0] + ev[1]:
-        e.record(stream)              # creates the event handles the kernel launch records
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(K):
-        if i % E == 0:
-            step(ev, i // E)
-        else:
-            step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(*ev)]))
+    ms_step, dom_ms, NE, t_wall = timed(K, E, lambda i: 0)
 
     total_flop = float(sum(flops))
     value = total_flop / (ms_step * 1e-3) / 1e12
@@ -271,6 +306,25 @@ def main():
             "kernel": "layer %d: %s" % (dom + 1, convs[dom].describe()),
             "kernel_ms": round(dom_ms, 5), "kernel_launches_timed": NE, "algorithmic_bytes": alg_bytes,
             "hbm_GBs_algorithmic": round(alg_bytes / (dom_ms * 1e-3) / 1e9, 1)}
+
+    # Cold caches: rotate through sets totalling at least 2x the MALL, so
+    # each step's buffers were last touched several hundred MB earlier.
+    cold = None
+    if args.cold_steps > 0:
+        sb = set_bytes(sets[0])
+        nsets = max(2, -(-COLD_POOL_BYTES // sb))
+        while len(sets) < nsets:
+            sets.append(make_set(False))
+        for i in range(nsets):
+            step(sets[i])
+        torch.cuda.synchronize()
+        Kc = args.cold_steps
+        c_step, c_dom, c_ne, _ = timed(Kc, E, lambda i: (i + 1) % nsets)
+        c_ach = flops[dom] / (c_dom * 1e-3) / 1e12
+        cold = {"value": round(total_flop / (c_step * 1e-3) / 1e12, 4), "ms_per_step": round(c_step, 5),
+                "kernel_ms": round(c_dom, 5), "achieved": round(c_ach, 3), "frac": round(c_ach / PEAK_TFLOPS[dt], 4),
+                "hbm_GBs_algorithmic": round(alg_bytes / (c_dom * 1e-3) / 1e9, 1),
+                "kernel_launches_timed": c_ne, "steps": Kc, "buffer_sets": nsets, "bytes_per_set": sb}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -287,7 +341,7 @@ def main():
                    "layers": [c.describe() for c in convs], "useful_gflop_per_step": round(total_flop / 1e9, 4),
                    "wall_s_timed": round(t_wall, 4), "parallelism": "single GPU",
                    "weight_prepack": prepack},
-        "roofline": roof, "cpu_baseline": cpu,
+        "roofline": roof, "cold": cold, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
