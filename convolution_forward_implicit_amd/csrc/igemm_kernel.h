@@ -99,15 +99,16 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
 }
 
 // Exact GELU, t * Phi(t), branch-free and short (the epilogue of a
-// thin-reduction conv is bound by it: ~70 cycles per wave-wide evaluation
-// on MI355X against ~110 for the erfc rational form it replaces).  With
-// a = min(|t|, 6): Phi(-a) = 2^R(a), R the degree-7 least-squares fit of
-// log2 Phi(-a) on [0, 6] at Chebyshev nodes, within 5.7e-6 (so Phi(-a)
-// within 4e-6 relative); one exp2, seven FMAs, no reciprocal.  t <= 0 gives
-// t Phi(t) = t Phi(-|t|), t > 0 gives t - t Phi(-t): neither form cancels.
-// Beyond |t| = 6 the clamped term is at most 6 Phi(-6) = 6e-9, so the
-// result stays within 6e-9 absolute of the exact value there (+inf maps to
-// +inf); NaN propagates.
+// thin-reduction conv is bound by it).  With a = min(|t|, 6):
+// Phi(-a) = 2^R(a), R the degree-7 least-squares fit of log2 Phi(-a) on
+// [0, 6] at Chebyshev nodes, within 5.7e-6 (so Phi(-a) within 4e-6
+// relative); one exp2, seven FMAs, no reciprocal.  The result is t times
+// Phi(t) = 1 - Phi(-|t|) for t >= +0 and Phi(-|t|) for t <= -0, the choice
+// made from t's sign bit by a bit-field select (no compare, so no
+// condition-register hazard): neither form cancels.  Beyond |t| = 6 the
+// clamped Phi(-6) = 1e-9 leaves an absolute error below 1e-9 |t|.  NaN
+// propagates through the product, +inf maps to +inf and -inf to -inf
+// (t * Phi(-6)).
 __device__ __forceinline__ float gelu_erf(float v)
 {
     const float a = fminf(fabsf(v), 6.0f);
@@ -119,9 +120,10 @@ __device__ __forceinline__ float gelu_erf(float v)
     r = fmaf(r, a, -4.584099095e-01f);
     r = fmaf(r, a, -1.151269077e+00f);
     r = fmaf(r, a, -9.999943512e-01f);
-    const float h = __builtin_amdgcn_fmed3f(v, -6.0f, 6.0f) * __builtin_amdgcn_exp2f(r);
-    const float g = v > 0.f ? v - h : h;
-    return v != v ? v : g;
+    const float p = __builtin_amdgcn_exp2f(r);                                   // Phi(-|v|)
+    const uint32_t neg = (uint32_t)((int32_t)__float_as_uint(v) >> 31);          // all ones iff sign set
+    const uint32_t q = (neg & __float_as_uint(p)) | (~neg & __float_as_uint(1.0f - p));
+    return v * __uint_as_float(q);
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);

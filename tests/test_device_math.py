@@ -27,9 +27,17 @@ def _device_gelu_f32(v):
     r = np.full(v.shape, c[0], dtype=np.float32)
     for k in c[1:]:   # fmaf: one rounding of the exact a*r + k
         r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
-    e = np.exp2(r.astype(np.float64)).astype(np.float32)
-    h = (np.clip(v, f(-6.0), f(6.0)) * e).astype(np.float32)
-    return np.where(v > 0, (v - h).astype(np.float32), h)
+    p = np.exp2(r.astype(np.float64)).astype(np.float32)
+    q = np.where(np.signbit(v), p, (f(1.0) - p).astype(np.float32))
+    return (v * q).astype(np.float32)
+
+
+def test_device_gelu_special_values():
+    v = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e30], dtype=np.float32)
+    g = _device_gelu_f32(v)
+    assert np.isnan(g[0]) and g[1] == np.inf and g[2] == -np.inf
+    assert g[3] == 0.0 and g[4] == 0.0
+    assert g[5] == np.float32(1e30)
 
 
 def test_device_gelu_polynomial_accuracy():
@@ -37,10 +45,12 @@ def test_device_gelu_polynomial_accuracy():
     exact = np.array([0.5 * float(x) * math.erfc(-float(x) / math.sqrt(2.0)) for x in t.astype(np.float64)])
     got = _device_gelu_f32(t).astype(np.float64)
     err = np.abs(got - exact)
-    # relative accuracy wherever the value is not tiny, absolute where it is
+    # relative accuracy wherever the value is not tiny; where it is (the
+    # negative tail, Phi clamped at Phi(-6) = 1e-9 beyond |t| = 6) within
+    # 1e-9 |t|, far inside the error bound the parity tests grade with
     big = np.abs(exact) > 1e-6
     assert np.max(err[big] / np.abs(exact[big])) < 1.2e-5
-    assert np.max(err[~big]) < 1e-8
+    assert np.max(err[~big] / np.maximum(np.abs(t[~big].astype(np.float64)), 1.0)) < 1.1e-9
     # the fit itself (not the float32 evaluation): log2 Phi(-a) within 6e-6 on [0, 6]
     a = np.linspace(0.0, 6.0, 60001)
     c = _device_gelu_coefficients()
