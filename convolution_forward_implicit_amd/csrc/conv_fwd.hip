@@ -202,6 +202,8 @@ const TileCfg kCfgs[] = {
     PATCH(8, 32, 64, 16, 2, 10, 34, 9, 0),
     PATCH(8, 32, 64, 16, 3, 10, 34, 9, 0),
     PATCH(8, 32, 32, 16, 2, 12, 36, 9, 0),
+    PATCH(16, 32, 32, 16, 2, 20, 36, 9, 0),
+    PATCH(16, 32, 32, 16, 2, 20, 36, 9, 1),
     PATCH(8, 32, 32, 16, 3, 12, 36, 9, 0),
     PATCH(8, 32, 64, 32, 2, 10, 34, 9, 0),
     PATCH(16, 16, 64, 16, 2, 18, 18, 9, 0),
