@@ -496,17 +496,23 @@ igemm_dma_kernel(DmaParams dp)
         }
     }
 
+    // A reduction group of one wave loads and reads only its own stages: its
+    // own vmcnt wait then suffices (the loads' LDS writes are complete when
+    // the count drops, and it read the buffer it refills before issuing the
+    // loads), so its steps need no workgroup barrier and the groups' SIMDs
+    // run out of lockstep.
+    constexpr bool STEP_BARRIER = S::NW > 1;
     for (int it = 0; it < nkh - 1; ++it) {
         if (it + NS - 2 < nkh) wait_vmcnt<S::L * (NS - 2)>();
         else wait_vmcnt<0>();
-        __syncthreads();                        // step it is in LDS for every wave
+        if constexpr (STEP_BARRIER) __syncthreads();   // step it is in LDS for every wave
         const bool more = it + NS - 1 < nkh;    // the buffer it refills was read in step it-1
         if (more) prep((kstart + it + NS - 1) * S::BK);
         compute(it % NS, more ? (it + NS - 1) % NS : -1);
     }
     // last step: nothing left to load
     wait_vmcnt<0>();
-    __syncthreads();
+    if constexpr (STEP_BARRIER) __syncthreads();
     // Bias of the lane's output channels (see the epilogue for the layout),
     // loaded here so that the last step's products hide its latency.
     float bias_v[S::BIAS_LDS ? 1 : S::NI][RUNS][4];
