@@ -181,6 +181,14 @@ struct TileCfg {
                 : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4"),       \
             0, 0, 0, 0, 0, 0, 4}
 
+#define DMA4F(DT, BM, BN, NS, MF, KSUB, FL)                                              \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), 1, 1, 16 / (DT ? 2 : 4), NS,  \
+            DmaShape<DT, BM, BN, 1, 1, NS, MF, KSUB, 4>::LDS_BYTES,                       \
+            &launch_dma<DT, BM, BN, 1, 1, NS, MF, KSUB, 4, FL>,                          \
+            (DT ? "bf16_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4_f" #FL  \
+                : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4_f" #FL), \
+            0, 0, 0, 0, 0, 0, 4}
+
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
 // filter taps per depth tap.
@@ -242,6 +250,7 @@ const TileCfg kCfgs[] = {
     DMA2(0, 64, 32, 4, 1, 2, 16, 1),
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
     DMA4(0, 48, 48, 2, 16, 1),
+    DMA4F(0, 48, 48, 2, 16, 1, 4),
     DMA2(0, 48, 96, 1, 2, 2, 16, 2),
     DMA4(0, 32, 32, 2, 16, 1),
     DMA2(1, 128, 64, 2, 2, 2, 32, 1),
