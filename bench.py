@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,15 +49,20 @@ METRIC = "conv fwd useful TFLOP/s and % of MFMA peak (Whisper frontend, grouped 
 DEFAULT_WORKLOAD = "whisper_frontend_f32_b1"
 
 
+_COMMENT = re.compile(rb"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash():
     """Hash of every source the HIP library is built from (kernels, host
-    code, selector coefficients)."""
+    code, selector coefficients), with comments and whitespace taken out so
+    that an edit that cannot change the compiled code keeps the hash."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "convolution_forward_implicit_amd", "csrc")
     for name in sorted(os.listdir(d)):
         with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+            code = b" ".join(_COMMENT.sub(b" ", f.read()).split())
+        h.update(name.encode())
+        h.update(code)
     return h.hexdigest()[:16]
 
 

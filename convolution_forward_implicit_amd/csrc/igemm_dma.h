@@ -163,9 +163,10 @@ igemm_dma_kernel(DmaParams dp)
     const int lane = tid & 63;
     // With KG > 1 the workgroup is KG groups of WM x WN waves that split the
     // reduction: group kg runs K-steps kg*nkh .. kg*nkh + nkh - 1 (steps past
-    // the end load zeros) through its own LDS stages, and groups 1 .. KG-1
-    // hand their partial tiles to group 0 through LDS at the end, which adds
-    // them in group order (a fixed order, so the sum is deterministic).  KG
+    // the end load zeros) through its own LDS stages; at the end every group
+    // writes its partial tile to LDS and all waves share the epilogue, which
+    // adds the partials in group order (a fixed order, so the sum is
+    // deterministic).  KG
     // times the waves per tile, 1/KG of the serial K-steps each: it pays for
     // problems with few output tiles and a long reduction (KG = 2: measured
     // 10-15% on 7x7 and 14x14 maps with 256-512 channels).  KG = 4 with one
