@@ -93,6 +93,9 @@ void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStre
     pp.pw = (TW - 1) * kp.sw + (kp.X - 1) * kp.dw + 1;
     pp.fd_pw = make_fastdiv(pp.pw);
     pp.fd_taps = make_fastdiv(kp.Y * kp.X);
+    pp.fd_tw = make_fastdiv(pp.tiles_w);
+    pp.fd_th = make_fastdiv(pp.tiles_h);
+    pp.fd_N = make_fastdiv(kp.N);
     const dim3 g(grid), b(256);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
@@ -322,8 +325,12 @@ const CostCoef *coef_of(const TileCfg &c)
     return nullptr;
 }
 
+// Division by d >= 1 as a multiply-high and shift (exact for 0 <= n < 2^31).
+// A zero-sized dimension (an empty batch has no output rows, so no tiles)
+// gets the divisor 1: such a plan launches nothing.
 FastDiv make_fastdiv(int d)
 {
+    if (d < 1) d = 1;
     FastDiv f;
     uint32_t s = 0;
     while ((1ull << s) < (uint64_t)d) ++s;
@@ -617,6 +624,8 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     kp.fd_C = make_fastdiv(kp.C);
     kp.fd_X = make_fastdiv(kp.X);
     kp.fd_Y = make_fastdiv(kp.Y);
+    kp.fd_tn = make_fastdiv(kp.tiles_n);
+    kp.fd_tm = make_fastdiv(kp.tiles_m);
     const double grid = tiles_of(c, d, out);
     if (grid >= 2147483647.0) {
         delete pl;

@@ -155,6 +155,18 @@ igemm_dma_kernel(DmaParams dp)
     using AccT = typename std::conditional<MF == 32, f32x16_t, f32x4_t>::type;
     using T = typename S::T;
     const KParams &p = dp.k;
+    // Fetch every argument the prologue reads in one batch at entry.  Left
+    // to itself the compiler issues each scalar argument load in the block
+    // of its first use, and the prologue then waits for three or four
+    // argument fetches one after another.
+    asm volatile("" ::"s"(gridDim.x), "s"(p.x), "s"(p.w), "s"(dp.x_bytes), "s"(dp.w_bytes), "s"(p.G), "s"(p.C),
+                 "s"(p.K), "s"(p.Di), "s"(p.Hi), "s"(p.Wi), "s"(p.Y), "s"(p.X), "s"(p.sd), "s"(p.sh),
+                 "s"(p.sw), "s"(p.pd), "s"(p.ph), "s"(p.pw), "s"(p.dd), "s"(p.dh));
+    asm volatile("" ::"s"(p.dw), "s"(p.Do), "s"(p.Ho), "s"(p.Wo), "s"(p.M), "s"(p.Kred),
+                 "s"(p.tiles_m), "s"(p.tiles_n), "s"(p.fd_Wo.m), "s"(p.fd_Wo.s), "s"(p.fd_Ho.m),
+                 "s"(p.fd_Ho.s), "s"(p.fd_Do.m), "s"(p.fd_Do.s), "s"(p.fd_C.m), "s"(p.fd_C.s),
+                 "s"(p.fd_X.m), "s"(p.fd_X.s), "s"(p.fd_Y.m), "s"(p.fd_Y.s), "s"(p.fd_Wo.d),
+                 "s"(p.out_vec), "s"(p.fd_tn.m), "s"(p.fd_tn.s), "s"(p.fd_tm.m), "s"(p.fd_tm.s));
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem;
@@ -188,10 +200,10 @@ igemm_dma_kernel(DmaParams dp)
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = nb >> 3, rem = nb & 7;
     int bid = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    const int n_tile = bid % p.tiles_n;
-    bid /= p.tiles_n;
-    const int m_tile = bid % p.tiles_m;
-    const int g = bid / p.tiles_m;
+    const int q_n = fdiv(bid, p.fd_tn);
+    const int n_tile = bid - q_n * p.tiles_n;
+    const int g = fdiv(q_n, p.fd_tm);
+    const int m_tile = q_n - g * p.tiles_m;
     const int m0 = m_tile * BM;
     const int n0 = n_tile * BN;
 

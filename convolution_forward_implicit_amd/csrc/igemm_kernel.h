@@ -66,6 +66,7 @@ struct KParams {
     int gelu;
     int out_vec;        // K % (16 / sizeof(out)) == 0: whole-vector stores
     FastDiv fd_Wo, fd_Ho, fd_Do, fd_C, fd_X, fd_Y;
+    FastDiv fd_tn, fd_tm;   // tiles_n, tiles_m
 };
 
 template <int BYTES> struct RawVec;

@@ -41,6 +41,7 @@ struct PatchParams {
     int tiles_h, tiles_w;   // boxes per output plane
     int ph, pw;             // patch rows and columns of this problem
     FastDiv fd_pw, fd_taps;
+    FastDiv fd_tw, fd_th, fd_N;   // tiles_w, tiles_h, N
 };
 
 template <int TH, int TW, int BN, int CC, int NS, int PHMAX, int PWMAX, int TAPMAX, int PAD>
@@ -75,6 +76,18 @@ patch_conv_kernel(PatchParams pp)
 {
     using S = PatchShape<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD>;
     const KParams &p = pp.k;
+    // Fetch every argument the prologue reads in one batch at entry (left to
+    // itself the compiler spreads the scalar argument loads over the blocks
+    // of their first use, and the prologue waits for each in turn).
+    asm volatile("" ::"s"(gridDim.x), "s"(p.x), "s"(p.w), "s"(pp.x_bytes), "s"(pp.w_bytes),
+                 "s"(p.tiles_n), "s"(pp.tiles_w), "s"(pp.tiles_h), "s"(p.Do), "s"(p.N), "s"(p.G),
+                 "s"(p.C), "s"(p.K), "s"(p.Di), "s"(p.Hi), "s"(p.Wi), "s"(p.Z), "s"(p.Y), "s"(p.X));
+    asm volatile("" ::"s"(p.sd), "s"(p.sh), "s"(p.sw), "s"(p.pd), "s"(p.ph), "s"(p.pw), "s"(p.dd),
+                 "s"(p.dh), "s"(p.dw), "s"(p.Kred), "s"(pp.ph), "s"(pp.pw), "s"(pp.fd_pw.m),
+                 "s"(pp.fd_pw.s), "s"(pp.fd_taps.m), "s"(pp.fd_taps.s));
+    asm volatile("" ::"s"(p.fd_tn.m), "s"(p.fd_tn.s), "s"(pp.fd_tw.m), "s"(pp.fd_tw.s),
+                 "s"(pp.fd_th.m), "s"(pp.fd_th.s), "s"(p.fd_Do.m), "s"(p.fd_Do.s), "s"(pp.fd_N.m),
+                 "s"(pp.fd_N.s));
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[S::LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem;
@@ -88,12 +101,16 @@ patch_conv_kernel(PatchParams pp)
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = nb >> 3, rem = nb & 7;
     int bid = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    const int n_tile = bid % p.tiles_n; bid /= p.tiles_n;
-    const int bw_ = bid % pp.tiles_w; bid /= pp.tiles_w;
-    const int bh_ = bid % pp.tiles_h; bid /= pp.tiles_h;
-    const int od = bid % p.Do; bid /= p.Do;
-    const int nimg = bid % p.N;
-    const int g = bid / p.N;
+    int qt = fdiv(bid, p.fd_tn);
+    const int n_tile = bid - qt * p.tiles_n; bid = qt;
+    qt = fdiv(bid, pp.fd_tw);
+    const int bw_ = bid - qt * pp.tiles_w; bid = qt;
+    qt = fdiv(bid, pp.fd_th);
+    const int bh_ = bid - qt * pp.tiles_h; bid = qt;
+    qt = fdiv(bid, p.fd_Do);
+    const int od = bid - qt * p.Do; bid = qt;
+    const int g = fdiv(bid, pp.fd_N);
+    const int nimg = bid - g * p.N;
     const int oh0 = bh_ * TH, ow0 = bw_ * TW;
     const int n0 = n_tile * BN;
 
