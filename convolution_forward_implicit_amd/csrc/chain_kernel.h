@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(256) chain_kernel(ChainParams cp)
                 for (int e = 0; e < 4; ++e) {
                     float t = acc1[mb][nb3][hh * 4 + e];
                     if constexpr (BIAS) t += bias_lds[ch + e];
-                    if constexpr (GELU) t = gelu_erf(t);
+                    if constexpr (GELU) t = gelu_erf_bf16out(t);
                     v[e] = inside ? t : 0.f;
                 }
                 uint2 pk;
@@ -300,7 +300,7 @@ __global__ void __launch_bounds__(256) chain_kernel(ChainParams cp)
                 for (int e = 0; e < 4; ++e) {
                     float t = acc2[mb][nb3][hh * 4 + e];
                     if constexpr (BIAS) t += bias_lds[K + ch + e];
-                    if constexpr (GELU) t = gelu_erf(t);
+                    if constexpr (GELU) t = gelu_erf_bf16out(t);
                     v[e] = t;
                 }
                 uint2 pk;

@@ -254,7 +254,7 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
                     for (int e = 0; e < 4; ++e) {
                         float t = acc[mb][j][hh * 4 + e];
                         if constexpr (BIAS) t += bias_lds[ch + e];
-                        if constexpr (GELU) t = gelu_erf(t);
+                        if constexpr (GELU) t = gelu_erf_bf16out(t);
                         v[e] = inside ? t : 0.f;
                     }
                     uint2 pk;
@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
                     for (int e = 0; e < 4; ++e) {
                         float t = acc2[mb][j][hh * 4 + e];
                         if constexpr (BIAS) t += bias_lds[K + ch + e];
-                        if constexpr (GELU) t = gelu_erf(t);
+                        if constexpr (GELU) t = gelu_erf_bf16out(t);
                         v[e] = t;
                     }
                     uint2 pk;

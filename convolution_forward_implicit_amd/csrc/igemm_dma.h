@@ -589,7 +589,7 @@ igemm_dma_kernel(DmaParams dp)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float t = sum[e] + bv[e];
-                    if constexpr (GELU) t = gelu_erf(t);
+                    if constexpr (GELU) t = DT == 1 ? gelu_erf_bf16out(t) : gelu_erf(t);
                     v[q4 * 4 + e] = t;
                 }
             }
@@ -646,7 +646,7 @@ igemm_dma_kernel(DmaParams dp)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[i][j][h * 4 + e] + bv[e];
-                    if constexpr (GELU) v[e] = gelu_erf(v[e]);
+                    if constexpr (GELU) v[e] = DT == 1 ? gelu_erf_bf16out(v[e]) : gelu_erf(v[e]);
                 }
                 if constexpr (DT == 1) {
                     uint2 pk;

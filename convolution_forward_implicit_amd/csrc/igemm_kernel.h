@@ -127,6 +127,30 @@ __device__ __forceinline__ float gelu_erf(float v)
     return v * __uint_as_float(q);
 }
 
+// GELU for results that are then rounded to bfloat16 (8 significant bits).
+// Same t * Phi(t), cut to the output's precision: R is the degree-5
+// least-squares fit of log2 Phi(-a) on [0, 6] at Chebyshev nodes, within
+// 5.9e-4 (Phi(-a) within 4.1e-4 relative, a tenth of the output's rounding
+// step), and t * Phi(t) is formed as t/2 + |t| (1/2 - Phi(-|t|)), one fused
+// multiply-add with no sign test.  Four vector operations fewer per value
+// than gelu_erf.  For t < 0 the two terms nearly cancel, so the rounding of
+// 1/2 - Phi(-|t|) leaves an absolute error up to 2^-25 |t|: half an fp32
+// rounding of t itself, inside the error that the fp32 sum producing t
+// already carries.  NaN propagates, +inf maps to +inf, -inf to NaN (as
+// t/2 * erfc(-t/sqrt 2) does).
+__device__ __forceinline__ float gelu_erf_bf16out(float v)
+{
+    const float a = fminf(fabsf(v), 6.0f);
+    float r = -1.975036866e-04f;
+    r = fmaf(r, a, 4.405779764e-03f);
+    r = fmaf(r, a, -4.251449928e-02f);
+    r = fmaf(r, a, -4.734477997e-01f);
+    r = fmaf(r, a, -1.143927097e+00f);
+    r = fmaf(r, a, -1.000582814e+00f);
+    const float h = 0.5f - __builtin_amdgcn_exp2f(r);   // 1/2 - Phi(-|v|)
+    return fmaf(fabsf(v), h, 0.5f * v);
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }

@@ -297,7 +297,7 @@ patch_conv_kernel(PatchParams pp)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[i][j][hh * 4 + e] + bv[e];
-                    if constexpr (GELU) v[e] = gelu_erf(v[e]);
+                    if constexpr (GELU) v[e] = gelu_erf_bf16out(v[e]);
                 }
                 uint2 pk;
                 pk.x = f32x2_to_bf16x2(v[0], v[1]);
