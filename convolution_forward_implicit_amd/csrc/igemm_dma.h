@@ -570,36 +570,61 @@ igemm_dma_kernel(DmaParams dp)
                 }
             }
         __syncthreads();
-        for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
+        // A fixed number of vectors per thread, all read and computed before
+        // any is stored (indices past the tile are clamped for the reads and
+        // skipped for the stores), so the LDS reads of every vector are in
+        // flight together and the VALU work runs back to back.
+        constexpr int NV = BM * OVPR;
+        constexpr int ITERS = (NV + S::NT - 1) / S::NT;
+        constexpr int NQ = S::VEC / 4;
+        f32x4_t part[ITERS][NQ][KG], bv[ITERS][NQ];
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int idx0 = tid + it * S::NT;
+            const int idx = idx0 < NV ? idx0 : NV - 1;
+            const int row = idx / OVPR;
+            const int cv = idx % OVPR;
+#pragma unroll
+            for (int q4 = 0; q4 < NQ; ++q4) {
+#pragma unroll
+                for (int g2 = 0; g2 < KG; ++g2)
+                    part[it][q4][g2] = *reinterpret_cast<const f32x4_t *>(pt + (g2 * BM + row) * S::LDF + cv * S::VEC + q4 * 4);
+                bv[it][q4] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS)
+                    bv[it][q4] = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + (cv * S::VEC + q4 * 4) * 4);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every read issued before the arithmetic
+        float v[ITERS][S::VEC];
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it)
+#pragma unroll
+            for (int q4 = 0; q4 < NQ; ++q4) {
+                f32x4_t sum = part[it][q4][0];
+#pragma unroll
+                for (int g2 = 1; g2 < KG; ++g2) sum += part[it][q4][g2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float t = sum[e] + bv[it][q4][e];
+                    if constexpr (GELU) t = DT == 1 ? gelu_erf_bf16out(t) : gelu_erf(t);
+                    v[it][q4 * 4 + e] = t;
+                }
+            }
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int idx = tid + it * S::NT;
             const int row = idx / OVPR;
             const int cv = idx % OVPR;
             const int m = m0 + row;
             const int n = n0 + cv * S::VEC;
-            if (m >= p.M || n >= p.K) continue;
-            float v[S::VEC];
-#pragma unroll
-            for (int q4 = 0; q4 < S::VEC / 4; ++q4) {
-                f32x4_t sum = *reinterpret_cast<const f32x4_t *>(pt + row * S::LDF + cv * S::VEC + q4 * 4);
-#pragma unroll
-                for (int g2 = 1; g2 < KG; ++g2)
-                    sum += *reinterpret_cast<const f32x4_t *>(pt + (g2 * BM + row) * S::LDF + cv * S::VEC + q4 * 4);
-                f32x4_t bv = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (BIAS)
-                    bv = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + (cv * S::VEC + q4 * 4) * 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float t = sum[e] + bv[e];
-                    if constexpr (GELU) t = DT == 1 ? gelu_erf_bf16out(t) : gelu_erf(t);
-                    v[q4 * 4 + e] = t;
-                }
-            }
+            if (idx >= NV || m >= p.M || n >= p.K) continue;
             T *dst = yg + (size_t)m * GK + n;
             if constexpr (DT == 1) {
                 uint4 pk;
-                pk.x = f32x2_to_bf16x2(v[0], v[1]);
-                pk.y = f32x2_to_bf16x2(v[2], v[3]);
-                pk.z = f32x2_to_bf16x2(v[4], v[5]);
-                pk.w = f32x2_to_bf16x2(v[6], v[7]);
+                pk.x = f32x2_to_bf16x2(v[it][0], v[it][1]);
+                pk.y = f32x2_to_bf16x2(v[it][2], v[it][3]);
+                pk.z = f32x2_to_bf16x2(v[it][4], v[it][5]);
+                pk.w = f32x2_to_bf16x2(v[it][6], v[it][7]);
                 if (p.out_vec) {
                     *reinterpret_cast<uint4 *>(dst) = pk;
                 } else {
@@ -609,10 +634,10 @@ igemm_dma_kernel(DmaParams dp)
                 }
             } else {
                 if (p.out_vec) {
-                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{v[0], v[1], v[2], v[3]};
+                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{v[it][0], v[it][1], v[it][2], v[it][3]};
                 } else {
                     const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
-                    for (int e = 0; e < lim; ++e) dst[e] = v[e];
+                    for (int e = 0; e < lim; ++e) dst[e] = v[it][e];
                 }
             }
         }
@@ -661,20 +686,40 @@ igemm_dma_kernel(DmaParams dp)
     }
     __syncthreads();
 
-    for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
-        const int row = idx / OVPR;
-        const int cv = idx % OVPR;
-        const int m = m0 + row;
-        const int n = n0 + cv * S::VEC;
-        if (m >= p.M || n >= p.K) continue;
-        const T *src = Cs + row * S::LDC + cv * S::VEC;
-        T *dst = yg + (size_t)m * GK + n;
-        if (p.out_vec) {
-            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-        } else {
+    if (!p.out_vec) {   // K not a whole number of vectors: element stores
+        for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
+            const int row = idx / OVPR;
+            const int cv = idx % OVPR;
+            const int m = m0 + row;
+            const int n = n0 + cv * S::VEC;
+            if (m >= p.M || n >= p.K) continue;
+            const T *src = Cs + row * S::LDC + cv * S::VEC;
+            T *dst = yg + (size_t)m * GK + n;
             const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
             for (int e = 0; e < lim; ++e) dst[e] = src[e];
         }
+        return;
+    }
+    // Whole 16-byte vectors: every read from LDS is issued before any store,
+    // so the reads' latency is paid once (indices past the tile are clamped
+    // for the reads and skipped for the stores).
+    constexpr int NV = BM * OVPR;
+    constexpr int ITERS = (NV + S::NT - 1) / S::NT;
+    i32x4_t val[ITERS];   // (a native vector type: an array of uint4 is kept in scratch)
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int idx0 = tid + it * S::NT;
+        const int idx = idx0 < NV ? idx0 : NV - 1;
+        val[it] = *reinterpret_cast<const i32x4_t *>(Cs + (idx / OVPR) * S::LDC + (idx % OVPR) * S::VEC);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int idx = tid + it * S::NT;
+        const int m = m0 + idx / OVPR;
+        const int n = n0 + (idx % OVPR) * S::VEC;
+        if (idx < NV && m < p.M && n < p.K)
+            *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
     }
 }
 
