@@ -310,20 +310,42 @@ patch_conv_kernel(PatchParams pp)
     uint16_t *__restrict__ yg = reinterpret_cast<uint16_t *>(p.y) + g * p.K;
     const int GK = p.G * p.K;
     constexpr int OVPR = BN / 8;
-    for (int idx = tid; idx < S::BM * OVPR; idx += S::NT) {
-        const int row = idx / OVPR;
-        const int cv = idx % OVPR;
-        const int oh = oh0 + row / TW, ow = ow0 + row % TW;
-        const int n = n0 + cv * 8;
-        if (oh >= p.Ho || ow >= p.Wo || n >= p.K) continue;
-        const int m = ((nimg * p.Do + od) * p.Ho + oh) * p.Wo + ow;
-        const uint16_t *src = Cs + row * S::LDC + cv * 8;
-        uint16_t *dst = yg + (size_t)m * GK + n;
-        if (p.out_vec) {
-            *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-        } else {
+    if (!p.out_vec) {   // K not a whole number of vectors: element stores
+        for (int idx = tid; idx < S::BM * OVPR; idx += S::NT) {
+            const int row = idx / OVPR;
+            const int cv = idx % OVPR;
+            const int oh = oh0 + row / TW, ow = ow0 + row % TW;
+            const int n = n0 + cv * 8;
+            if (oh >= p.Ho || ow >= p.Wo || n >= p.K) continue;
+            const int m = ((nimg * p.Do + od) * p.Ho + oh) * p.Wo + ow;
+            const uint16_t *src = Cs + row * S::LDC + cv * 8;
+            uint16_t *dst = yg + (size_t)m * GK + n;
             const int lim = (p.K - n) < 8 ? (p.K - n) : 8;
             for (int e = 0; e < lim; ++e) dst[e] = src[e];
+        }
+        return;
+    }
+    // Whole 16-byte vectors: every read from LDS is issued before any store
+    // (a native vector type, which stays in registers).
+    constexpr int NV = S::BM * OVPR;
+    constexpr int ITERS = (NV + S::NT - 1) / S::NT;
+    i32x4_t val[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int idx0 = tid + it * S::NT;
+        const int idx = idx0 < NV ? idx0 : NV - 1;
+        val[it] = *reinterpret_cast<const i32x4_t *>(Cs + (idx / OVPR) * S::LDC + (idx % OVPR) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int idx = tid + it * S::NT;
+        const int row = idx / OVPR;
+        const int oh = oh0 + row / TW, ow = ow0 + row % TW;
+        const int n = n0 + (idx % OVPR) * 8;
+        if (idx < NV && oh < p.Ho && ow < p.Wo && n < p.K) {
+            const int m = ((nimg * p.Do + od) * p.Ho + oh) * p.Wo + ow;
+            *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
         }
     }
 }
