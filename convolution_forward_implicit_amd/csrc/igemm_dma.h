@@ -158,7 +158,10 @@ igemm_dma_kernel(DmaParams dp)
     // Fetch every argument the prologue reads in one batch at entry.  Left
     // to itself the compiler issues each scalar argument load in the block
     // of its first use, and the prologue then waits for three or four
-    // argument fetches one after another.
+    // argument fetches one after another.  (fd_Wo.d and out_vec arrive in
+    // the same wide loads as used fields; listing them keeps their registers
+    // from being reused by another load of the batch, which would need a
+    // wait in between.)
     asm volatile("" ::"s"(gridDim.x), "s"(p.x), "s"(p.w), "s"(dp.x_bytes), "s"(dp.w_bytes), "s"(p.G), "s"(p.C),
                  "s"(p.K), "s"(p.Di), "s"(p.Hi), "s"(p.Wi), "s"(p.Y), "s"(p.X), "s"(p.sd), "s"(p.sh),
                  "s"(p.sw), "s"(p.pd), "s"(p.ph), "s"(p.pw), "s"(p.dd), "s"(p.dh));
