@@ -1,11 +1,13 @@
-"""CPU build checks of the direct-to-LDS implicit-GEMM kernel (no GPU):
+"""CPU build checks of the direct-to-LDS kernels (no GPU):
 representative instantiations of every code path (wide-N tiles, four and
 two reduction groups, front-loaded loads, 16x16 and 32x32 bf16 blocks,
 fp32 blocks over two sub-slices; with and without the bias + GELU
-epilogue) are compiled for gfx950 and must use no scratch memory.  A helper
+epilogue; and the patch kernel's configurations) are compiled for gfx950
+and must use no scratch memory.  A helper
 lambda that the compiler leaves as a call passes its captures through
-scratch, which made such kernels 10-100x slower; register spills show up
-the same way."""
+scratch, which made such kernels 10-100x slower; an array of uint4 kept
+across the epilogue's LDS reads and stores landed there too; register
+spills show up the same way."""
 import os
 import re
 import shutil
@@ -32,12 +34,20 @@ INSTANCES = [
 ]
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
-def test_dma_kernels_use_no_scratch():
-    lines = ['#include "igemm_dma.h"', "namespace convfwd {"]
-    for inst in INSTANCES:
+# <TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD>
+PATCH_INSTANCES = [
+    "16, 32, 32, 16, 2, 20, 36, 9, 0",
+    "8, 32, 64, 16, 2, 10, 34, 9, 1",
+    "8, 32, 64, 16, 3, 10, 34, 9, 0",
+    "8, 32, 64, 32, 2, 10, 34, 9, 0",
+]
+
+
+def _resource_usage(header, kernel, params, instances):
+    lines = ['#include "%s"' % header, "namespace convfwd {"]
+    for inst in instances:
         for ep in ("true, true", "false, false"):
-            lines.append("template __global__ void igemm_dma_kernel<%s, %s>(DmaParams);" % (inst, ep))
+            lines.append("template __global__ void %s<%s, %s>(%s);" % (kernel, inst, ep, params))
     lines.append("}")
     d = tempfile.mkdtemp()
     try:
@@ -55,6 +65,17 @@ def test_dma_kernels_use_no_scratch():
     names = re.findall(r"Function Name: (\S+)", r.stdout)
     scratch = [int(v) for v in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stdout)]
     spills = [int(v) for v in re.findall(r"VGPRs Spill: (\d+)", r.stdout)]
-    assert len(names) == 2 * len(INSTANCES) == len(scratch) == len(spills), r.stdout[-2000:]
-    bad = [(n, s, v) for n, s, v in zip(names, scratch, spills) if s or v]
+    assert len(names) == 2 * len(instances) == len(scratch) == len(spills), r.stdout[-2000:]
+    return [(n, s, v) for n, s, v in zip(names, scratch, spills) if s or v]
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_dma_kernels_use_no_scratch():
+    bad = _resource_usage("igemm_dma.h", "igemm_dma_kernel", "DmaParams", INSTANCES)
+    assert not bad, bad
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_patch_kernels_use_no_scratch():
+    bad = _resource_usage("patch_kernel.h", "patch_conv_kernel", "PatchParams", PATCH_INSTANCES)
     assert not bad, bad
