@@ -60,13 +60,8 @@ class ConvFwd:
         self.y_shape = (p["N"],) + self.out_dims + (p["G"], p["K"])
 
     def useful_flop(self):
-        """2 * multiply-adds counting padded taps (the conv1d issue's way of
-        turning dispatch times into useful throughput)."""
-        p = self.problem
-        n = 2 * p["N"] * p["G"] * p["K"] * p["C"]
-        for v in self.out_dims + tuple(p["filt"]):
-            n *= v
-        return n
+        """2 * multiply-adds counting padded taps (the library's count)."""
+        return capi.conv_fwd_useful_flop(self._plan)
 
     def describe(self):
         return capi.conv_fwd_describe(self._plan)
@@ -140,16 +135,13 @@ class ConvChain:
         self.w1_shape = (p1["G"], p1["K"]) + tuple(p1["filt"]) + (p1["C"],)
         self.w2_shape = (p2["G"], p2["K"]) + tuple(p2["filt"]) + (p2["C"],)
         self.b_shape = (p1["G"], p1["K"])
-        Lo = (p2["in"][2] + 2 * p2["pad"][2] - p2["dil"][2] * (p2["filt"][2] - 1) - 1) // p2["stride"][2] + 1
-        self.y_shape = (p2["N"], 1, 1, Lo, p2["G"], p2["K"])
+        self.out_dims = capi.conv_chain_out_dims(self._plan)
+        self.y_shape = (p2["N"],) + self.out_dims + (p2["G"], p2["K"])
 
     def useful_flop(self):
-        """Both convs' 2 * multiply-adds, counting padded taps."""
-        n = 0
-        for p in (self.first, self.second):
-            o = (p["in"][2] + 2 * p["pad"][2] - p["dil"][2] * (p["filt"][2] - 1) - 1) // p["stride"][2] + 1
-            n += 2 * p["N"] * p["K"] * p["C"] * p["filt"][2] * o
-        return n
+        """Both convs' 2 * multiply-adds, counting padded taps (the
+        library's count)."""
+        return capi.conv_chain_useful_flop(self._plan)
 
     def describe(self):
         return capi.conv_chain_describe(self._plan)

@@ -24,11 +24,11 @@ CONV_ERR_NOMEM = 4
 STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTED",
                 3: "CONV_ERR_HIP", 4: "CONV_ERR_NOMEM"}
 
-EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims",
+EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims", "conv_fwd_useful_flop",
             "conv_fwd_run", "conv_fwd_run_events", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
             "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error",
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
-            "conv_chain_describe", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
+            "conv_chain_describe", "conv_chain_out_dims", "conv_chain_useful_flop", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
             "conv_chain_run_packed_events", "conv_bwd_data_create", "conv_bwd_data_workspace_bytes",
             "conv_bwd_data_run", "conv_bwd_data_destroy", "conv_bwd_data_describe", "conv_bwd_weight_create",
             "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_run", "conv_bwd_weight_destroy",
@@ -71,6 +71,12 @@ def lib():
         L.conv_fwd_create_with_config.restype = ctypes.c_int
         L.conv_fwd_out_dims.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
         L.conv_fwd_out_dims.restype = ctypes.c_int
+        L.conv_fwd_useful_flop.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_fwd_useful_flop.restype = ctypes.c_int
+        L.conv_chain_out_dims.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_chain_out_dims.restype = ctypes.c_int
+        L.conv_chain_useful_flop.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+        L.conv_chain_useful_flop.restype = ctypes.c_int
         L.conv_fwd_run.argtypes = [P, P, P, P, P, P]
         L.conv_fwd_run.restype = ctypes.c_int
         L.conv_fwd_run_events.argtypes = [P, P, P, P, P, P, P, P]
@@ -164,6 +170,24 @@ def conv_fwd_out_dims(plan):
     out = (ctypes.c_int64 * 3)()
     _check(lib().conv_fwd_out_dims(plan, out))
     return tuple(int(v) for v in out)
+
+
+def conv_fwd_useful_flop(plan):
+    n = ctypes.c_int64()
+    _check(lib().conv_fwd_useful_flop(plan, ctypes.byref(n)))
+    return n.value
+
+
+def conv_chain_out_dims(plan):
+    out = (ctypes.c_int64 * 3)()
+    _check(lib().conv_chain_out_dims(plan, out))
+    return tuple(int(v) for v in out)
+
+
+def conv_chain_useful_flop(plan):
+    n = ctypes.c_int64()
+    _check(lib().conv_chain_useful_flop(plan, ctypes.byref(n)))
+    return n.value
 
 
 def conv_fwd_run(plan, x, w, bias, y, stream=0):

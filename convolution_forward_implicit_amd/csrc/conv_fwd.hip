@@ -358,6 +358,7 @@ using namespace convfwd;
 
 struct conv_chain_plan {
     conv_fwd_desc_t first, second;
+    int64_t out1[3], out2[3];   // output extents of the two convs
     int64_t x_elems, w1_elems, w2_elems, b_elems, y_elems;
     ChainParams cp;  // pointers filled per run
     int grid;
@@ -668,6 +669,15 @@ conv_status_t conv_fwd_out_dims(const conv_fwd_plan_t *plan, int64_t out[3])
     return CONV_OK;
 }
 
+conv_status_t conv_fwd_useful_flop(const conv_fwd_plan_t *plan, int64_t *flop)
+{
+    if (!plan || !flop) return fail(CONV_ERR_INVALID_ARG, "NULL argument");
+    const conv_fwd_desc_t &d = plan->desc;
+    *flop = 2 * d.N * d.G * d.K * d.C * plan->out[0] * plan->out[1] * plan->out[2] * d.filt[0] * d.filt[1] *
+            d.filt[2];
+    return CONV_OK;
+}
+
 static bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
 {
     if (!a || !b || an <= 0 || bn <= 0) return false;
@@ -746,6 +756,10 @@ conv_status_t conv_chain_create(const conv_fwd_desc_t *first, const conv_fwd_des
     if (!pl) return fail(CONV_ERR_NOMEM, "plan allocation failed");
     pl->first = a;
     pl->second = b;
+    for (int i = 0; i < 3; ++i) {
+        pl->out1[i] = o1[i];
+        pl->out2[i] = o2[i];
+    }
     pl->x_elems = a.N * a.in[2] * a.C;
     pl->w1_elems = a.K * 3 * a.C;
     pl->w2_elems = b.K * 3 * b.C;
@@ -905,6 +919,21 @@ conv_status_t conv_chain_run_packed(const conv_chain_plan_t *plan, const void *x
                                     const void *b2, void *y, void *stream)
 {
     return conv_chain_run_packed_events(plan, x, packed, b1, b2, y, stream, nullptr, nullptr);
+}
+
+conv_status_t conv_chain_out_dims(const conv_chain_plan_t *plan, int64_t out[3])
+{
+    if (!plan || !out) return fail(CONV_ERR_INVALID_ARG, "NULL argument");
+    for (int i = 0; i < 3; ++i) out[i] = plan->out2[i];
+    return CONV_OK;
+}
+
+conv_status_t conv_chain_useful_flop(const conv_chain_plan_t *plan, int64_t *flop)
+{
+    if (!plan || !flop) return fail(CONV_ERR_INVALID_ARG, "NULL argument");
+    const conv_fwd_desc_t &a = plan->first, &b = plan->second;
+    *flop = 2 * a.N * a.K * a.C * a.filt[2] * plan->out1[2] + 2 * b.N * b.K * b.C * b.filt[2] * plan->out2[2];
+    return CONV_OK;
 }
 
 void conv_chain_destroy(conv_chain_plan_t *plan) { delete plan; }

@@ -105,6 +105,12 @@ conv_status_t conv_fwd_create_with_config(const conv_fwd_desc_t *desc, int32_t c
 /* Writes (Do, Ho, Wo) of the plan's problem to out[3]. */
 conv_status_t conv_fwd_out_dims(const conv_fwd_plan_t *plan, int64_t out[3]);
 
+/* Writes the plan's useful work to *flop: 2 x the multiply-adds of the sum
+ * above, taps that fall in the zero padding included (the ExecuTorch conv1d
+ * issue, section "Measurements", turns dispatch times into GFLOP/s this way):
+ * 2 * N * G * K * C * Do*Ho*Wo * Z*Y*X.  INVALID_ARG for NULL arguments. */
+conv_status_t conv_fwd_useful_flop(const conv_fwd_plan_t *plan, int64_t *flop);
+
 /* Enqueues y = conv(x, w) (+ bias) (then GELU) on `stream` (a hipStream_t;
  * NULL = the null stream).  x, w, y: device pointers in the layouts above,
  * 16-byte aligned; bias: device pointer, must be NULL iff the plan has no
@@ -204,6 +210,13 @@ conv_status_t conv_chain_run_packed(const conv_chain_plan_t *plan, const void *x
 conv_status_t conv_chain_run_packed_events(const conv_chain_plan_t *plan, const void *x, const void *packed,
                                            const void *b1, const void *b2, void *y, void *stream,
                                            void *start_event, void *stop_event);
+
+/* Writes (1, 1, Lo) -- the extents of y, the second conv's output -- to
+ * out[3], and the useful work of both convs (2 x multiply-adds each, padded
+ * taps included, as conv_fwd_useful_flop) to *flop.  INVALID_ARG for NULL
+ * arguments. */
+conv_status_t conv_chain_out_dims(const conv_chain_plan_t *plan, int64_t out[3]);
+conv_status_t conv_chain_useful_flop(const conv_chain_plan_t *plan, int64_t *flop);
 
 /* Frees a chain plan (NULL is a no-op). */
 void conv_chain_destroy(conv_chain_plan_t *plan);

@@ -121,13 +121,3 @@ def round_to_bf16_bits(v):
 def bf16_bits_to_f64(bits):
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
-
-
-def ulp_distance_bf16(got_bits, ref_bits):
-    """Distance in bf16 ulps between two bf16 bit patterns (ordered-int
-    mapping), for reporting."""
-    def ordered(b):
-        b = np.asarray(b, dtype=np.uint16).astype(np.int32)
-        return np.where(b & 0x8000, 0x8000 - b, b)
-    return np.abs(ordered(got_bits) - ordered(ref_bits))
-

@@ -116,11 +116,11 @@ def workload(wid):
     return out
 
 
-def random_inputs(p, dtype, seed, has_bias, kind="float"):
+def random_inputs(p, dtype, seed, has_bias, kind="float", imax=2):
     """Inputs for an arbitrary problem: kind="float" draws x ~ U[-1,1),
     w ~ N(0, 1/sqrt(fan_in)), b ~ N(0, 0.02); kind="int" draws integers in
-    {-2..2} for x, w and b (sums stay far below 2^24, so any fp32 summation
-    order gives the exact result)."""
+    {-imax..imax} for x, w and b (with the default 2 the sums stay far below
+    2^24, so any fp32 summation order gives the exact result)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     Di, Hi, Wi = p["in"]
     Z, Y, X = p["filt"]
@@ -128,9 +128,9 @@ def random_inputs(p, dtype, seed, has_bias, kind="float"):
     ws = (p["G"], p["K"], Z, Y, X, p["C"])
     bs = (p["G"], p["K"])
     if kind == "int":
-        x = rng.integers(-2, 3, size=xs).astype(np.float32)
-        w = rng.integers(-2, 3, size=ws).astype(np.float32)
-        b = rng.integers(-2, 3, size=bs).astype(np.float32) if has_bias else None
+        x = rng.integers(-imax, imax + 1, size=xs).astype(np.float32)
+        w = rng.integers(-imax, imax + 1, size=ws).astype(np.float32)
+        b = rng.integers(-imax, imax + 1, size=bs).astype(np.float32) if has_bias else None
         return x, w, b
     x = _store(rng.uniform(-1.0, 1.0, size=xs), dtype)
     w = _store(rng.normal(0.0, 1.0 / np.sqrt(p["C"] * Z * Y * X), size=ws), dtype)

@@ -291,6 +291,52 @@ def test_chain_create_accepts_the_frontend_and_describes_it():
     assert capi.conv_chain_describe(None) == ""
 
 
+@pytest.mark.parametrize("N,L,C1", [(1, 3000, 80), (32, 3000, 80), (2, 301, 16), (3, 2, 128), (1, 1, 224)])
+def test_chain_out_dims_and_flop_come_from_the_library(N, L, C1):
+    """conv_chain_out_dims / conv_chain_useful_flop against the oracle's
+    extents of the two convs and the 2 x multiply-add count with padded taps
+    (per conv: 2 * N * K * C * taps * Lo); the binding sizes y from them."""
+    from convolution_forward_implicit_amd import ConvChain
+    p1 = sd.conv1d_problem(N, C1, 384, L, 3, 1, 1)
+    p2 = sd.conv1d_problem(N, 384, 384, L, 3, 2, 1)
+    a, b = desc_from_problem(p1, "bf16", True, True), desc_from_problem(p2, "bf16", True, True)
+    plan = capi.conv_chain_create(a, b)
+    try:
+        o1, o2 = ref.out_dims(p1), ref.out_dims(p2)
+        assert o1 == (1, 1, L)
+        assert capi.conv_chain_out_dims(plan) == o2
+        want = 2 * N * 384 * C1 * 3 * o1[2] + 2 * N * 384 * 384 * 3 * o2[2]
+        assert capi.conv_chain_useful_flop(plan) == want
+    finally:
+        capi.conv_chain_destroy(plan)
+    c = ConvChain(p1, p2, "bf16", True, True)
+    assert c.y_shape == (N,) + o2 + (1, 384)
+    assert c.useful_flop() == want
+    with pytest.raises(ConvError):
+        capi.conv_chain_out_dims(None)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
+def test_useful_flop_comes_from_the_library(wid):
+    """conv_fwd_useful_flop = 2 * N * G * K * C * prod(output extents) *
+    prod(filter) with the oracle's extents; the workloads' totals
+    (useful GFLOP 0.553, 1.880, 60.162, 7.399, 11.098)."""
+    total = 0
+    for p, hb, ge in sd.layers(wid):
+        plan = capi.conv_fwd_create(desc_from_problem(p, sd.dtype_of(wid), hb, ge))
+        try:
+            o = ref.out_dims(p)
+            want = 2 * p["N"] * p["G"] * p["K"] * p["C"] * o[0] * o[1] * o[2] * \
+                p["filt"][0] * p["filt"][1] * p["filt"][2]
+            assert capi.conv_fwd_useful_flop(plan) == want
+            total += want
+        finally:
+            capi.conv_fwd_destroy(plan)
+    assert round(total / 1e9, 3) == {1: 0.553, 2: 1.880, 3: 60.162, 4: 7.399, 5: 11.098}[wid]
+    with pytest.raises(ConvError):
+        capi.conv_fwd_useful_flop(None)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype="f32"), capi.CONV_ERR_UNSUPPORTED),
     (dict(C1=72), capi.CONV_ERR_UNSUPPORTED),          # not a multiple of 16

@@ -79,7 +79,7 @@ def assert_close(got, p, dtype, x, w, b, gelu, idx=None):
 
 # --------------------------------------------------------------------------
 # The five workloads at full size, in the launch configuration the benchmark
-# times (the selector's choice).
+# times (the selector's choice): every output element against the oracle.
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_workload_seeded_parity(dev, wid):
     W = sd.workload(wid)
@@ -87,31 +87,26 @@ def test_workload_seeded_parity(dev, wid):
     x = W["x"]
     for li, (p, hb, ge) in enumerate(W["layers"]):
         y, c = run(dev, p, dt, x, W["w"][li], W["b"][li], ge)
-        full = ref.useful_flop(p) < 2e9
-        idx = None if full else sample_indices(p, 4000, 100 + wid * 10 + li)
-        assert_close(host(y), p, dt, x, W["w"][li], W["b"][li], ge, idx)
+        st = assert_close(host(y), p, dt, x, W["w"][li], W["b"][li], ge)
+        assert st["n"] == int(np.prod(ref.shapes(p)[3]))
         x = host(y).astype(np.float32)   # next layer is graded on the device's own input
 
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_workload_integer_bit_exact(dev, wid):
+    """Integer-valued inputs at the workload shapes: every output element
+    bit for bit (bf16 against the one nearest-even rounding of the exact
+    sum)."""
     W = sd.workload(wid)
     dt = W["dtype"]
     for li, (p, hb, _) in enumerate(W["layers"]):
         x, w, b = sd.random_inputs(p, dt, 500 + wid * 10 + li, hb, kind="int")
         y, _ = run(dev, p, dt, x, w, b, False)
-        full = ref.useful_flop(p) < 2e9
-        idx = None if full else sample_indices(p, 4000, 7 + li)
-        r = ref.conv_fwd(p, x, w, b, False, want_absdot=False)
-        r = r.ravel() if idx is None else r.ravel()[idx]
+        r = ref.conv_fwd(p, x, w, b, False, want_absdot=False).ravel()
         if dt == "f32":
-            g = host(y).ravel()
-            g = g if idx is None else g[idx]
-            assert np.array_equal(g, r)
+            assert np.array_equal(host(y).ravel(), r)
         else:
-            g = bits(y).ravel()
-            g = g if idx is None else g[idx]
-            assert np.array_equal(g, check.round_to_bf16_bits(r))
+            assert np.array_equal(bits(y).ravel(), check.round_to_bf16_bits(r))
 
 
 # --------------------------------------------------------------------------
@@ -421,18 +416,48 @@ def test_chain_packed_no_bias_no_gelu_and_pack_layout(dev):
     assert np.array_equal(np.sort(key(nonzero)), np.sort(key(nat[(nat != 0).any(axis=1)])))
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_chain_workload_full_size_sampled(dev, packed):
-    """The batch-32 bf16 frontend at full size, in the launch the benchmark
-    times with --fused: 4000 random outputs plus borders against the oracle."""
+@pytest.fixture(scope="module")
+def chain_workload_oracle():
+    """The oracle's batch-32 bf16 frontend (h rounded to bf16 between the
+    convs), every output, computed once for both chain kernels."""
     W = sd.workload(3)
     (p1, _, _), (p2, _, _) = W["layers"]
+    return W, ref.conv_chain(p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_chain_workload_full_size(dev, packed, chain_workload_oracle):
+    """The batch-32 bf16 frontend at full size, in the launch the benchmark
+    times with --fused: every output against the oracle."""
+    W, (r, a2, cy) = chain_workload_oracle
+    (p1, _, _), (p2, _, _) = W["layers"]
     y, _ = run_chain(dev, p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True, packed)
-    idx = sample_indices(p2, 4000, 85)
-    r, a2, cy = ref.conv_chain_points(p1, p2, W["x"], W["w"][0], W["b"][0], W["w"][1], W["b"][1], True, idx)
-    st = check.check_chain(host(y).ravel()[idx], r, a2, cy, p1, p2, True)
+    st = check.check_chain(host(y), r, a2, cy, p1, p2, True)
     print("parity:", {k: v for k, v in st.items() if k != "limit"}, flush=True)
     assert st["ok"], {k: v for k, v in st.items() if k != "limit"}
+    assert st["n"] == r.size
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("N,L", [(32, 3000), (2, 301)])
+def test_chain_integer_h_rounding_bit_exact(dev, N, L, packed):
+    """Integer inputs wide enough that the intermediate h needs rounding:
+    x, w1, b1 in {-8..8} make conv1's exact sums often larger than 256, so
+    they have more than bf16's 8 significant bits and h is their one
+    nearest-even rounding (truncating h would change many of them).  w2, b2
+    in {-2..2}: conv2's terms are integers whose absolute sum stays below
+    2^24 (checked), so its fp32 sums are exact in any order and every bf16
+    output has one correct value.  (32, 3000) is the batch-32 frontend shape
+    the benchmark times with --fused."""
+    p1, p2 = _chain(N, L)
+    x, w1, b1 = sd.random_inputs(p1, "bf16", 88, True, kind="int", imax=8)
+    _, w2, b2 = sd.random_inputs(p2, "bf16", 89, True, kind="int")
+    h = ref.conv_fwd(p1, x, w1, b1, False, want_absdot=False)
+    assert np.mean(ref.round_bf16(h) != h) > 0.2          # rounding of h is exercised
+    y, _ = run_chain(dev, p1, p2, x, w1, b1, w2, b2, False, packed)
+    r, a2, _ = ref.conv_chain(p1, p2, x, w1, b1, w2, b2, False)
+    assert float(a2.max()) < 2.0 ** 24                      # conv2's fp32 sums are exact
+    assert np.array_equal(bits(y).ravel(), check.round_to_bf16_bits(r).ravel())
 
 
 def test_chain_empty_batch(dev):
@@ -510,19 +535,15 @@ def test_bwd_data_seeded_float_parity(dev, name, p, dt):
 
 
 @pytest.mark.parametrize("wid", [4, 5])
-def test_bwd_data_grouped_workloads_full_size_sampled(dev, wid):
-    """The grouped 2-D and dilated 3-D workload shapes at full size: 4000
-    random input-gradient elements plus borders against the oracle."""
+def test_bwd_data_grouped_workloads_full_size(dev, wid):
+    """The grouped 2-D and dilated 3-D workload shapes at full size: every
+    input-gradient element against the oracle."""
     W = sd.workload(wid)
     (p, _, _), = W["layers"]
     dy = _dy(p, "bf16", 95, "float")
     dx, _ = run_bwd_data(dev, p, "bf16", dy, W["w"][0])
-    xs = ref.shapes(p)[0]
-    rng = np.random.Generator(np.random.PCG64(96))
-    idx = np.unique(np.concatenate([rng.integers(0, int(np.prod(xs)), 4000),
-                                    np.arange(0, int(np.prod(xs)), int(np.prod(xs)) // 97)]))
-    r, a = ref.conv_bwd_data_points(p, dy, W["w"][0], idx)
-    st = check.check(host(dx).ravel()[idx], r, a, _terms(p["K"] * np.prod(p["filt"])), "bf16", False, False)
+    r, a = ref.conv_bwd_data(p, dy, W["w"][0])
+    st = check.check(host(dx), r, a, _terms(p["K"] * np.prod(p["filt"])), "bf16", False, False)
     print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
     assert st["ok"], st
 
@@ -608,17 +629,15 @@ def test_bwd_weight_seeded_float_parity(dev, name, p):
 
 
 @pytest.mark.parametrize("wid", [4, 5])
-def test_bwd_weight_grouped_workloads_full_size_sampled(dev, wid):
-    """The grouped workload shapes at full size: 2000 random weight-gradient
-    elements (each a sum over every output pixel) against the oracle."""
+def test_bwd_weight_grouped_workloads_full_size(dev, wid):
+    """The grouped workload shapes at full size: every weight-gradient
+    element (each a sum over every output pixel) against the oracle."""
     W = sd.workload(wid)
     (p, _, _), = W["layers"]
     dy = _dy(p, "bf16", 101, "float")
     dw, _ = run_bwd_weight(dev, p, W["x"], dy)
-    ws = ref.shapes(p)[1]
-    idx = np.unique(np.random.Generator(np.random.PCG64(102)).integers(0, int(np.prod(ws)), 2000))
-    r, a = ref.conv_bwd_weight_points(p, W["x"], dy, idx)
-    st = check.check(host(dw).ravel()[idx], r, a, _terms(_pixels(p)), "bf16", False, False)
+    r, a = ref.conv_bwd_weight(p, W["x"], dy)
+    st = check.check(host(dw), r, a, _terms(_pixels(p)), "bf16", False, False)
     print("parity:", {k: st[k] for k in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
     assert st["ok"], st
 
