@@ -13,14 +13,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "conv_fwd.hip")]
 LIB = os.path.join(HERE, "libconvfwd.so")
+# peak-rate probes (measured roofline denominators for the benchmark)
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "peak_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libconvprobe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = [HIPCC] + FLAGS + ["-o", LIB + ".tmp"] + SOURCES
+def _compile(sources, lib, verbose):
+    cmd = [HIPCC] + FLAGS + ["-o", lib + ".tmp"] + sources
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -30,7 +33,12 @@ def build(verbose: bool = False) -> str:
         print(out, file=sys.stderr)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed (%d)" % r.returncode)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False) -> str:
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    _compile(SOURCES, LIB, verbose)
     return LIB
 
 

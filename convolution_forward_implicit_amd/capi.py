@@ -309,3 +309,47 @@ def conv_bwd_weight_describe(plan):
 
 def conv_fwd_last_error():
     return lib().conv_fwd_last_error().decode()
+
+
+# ---- peak-rate probes (include/convprobe.h), used by the benchmark ---------
+PROBE_LIB_PATH = os.path.join(_HERE, "libconvprobe.so")
+PROBE_EXPORTED = ["conv_probe_threads", "conv_probe_mfma", "conv_probe_hbm_read"]
+_probe = None
+
+
+def probe_lib():
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError("peak-probe library not built: %s is missing "
+                              "(run python -m convolution_forward_implicit_amd.build)" % PROBE_LIB_PATH)
+        L = ctypes.CDLL(PROBE_LIB_PATH)
+        P = ctypes.c_void_p
+        L.conv_probe_threads.argtypes = []
+        L.conv_probe_threads.restype = ctypes.c_int32
+        L.conv_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                      ctypes.POINTER(ctypes.c_double)]
+        L.conv_probe_mfma.restype = ctypes.c_int32
+        L.conv_probe_hbm_read.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P]
+        L.conv_probe_hbm_read.restype = ctypes.c_int32
+        _probe = L
+    return _probe
+
+
+def conv_probe_threads():
+    return int(probe_lib().conv_probe_threads())
+
+
+def conv_probe_mfma(kind, iters, grid, sink, stream=0):
+    """Enqueues the MFMA probe; returns the useful FLOP of the launch."""
+    f = ctypes.c_double()
+    rc = probe_lib().conv_probe_mfma(int(kind), int(iters), int(grid), sink, stream, ctypes.byref(f))
+    if rc != 0:
+        raise RuntimeError("conv_probe_mfma failed: hipError %d" % rc)
+    return f.value
+
+
+def conv_probe_hbm_read(buf, nbytes, grid, sink, stream=0):
+    rc = probe_lib().conv_probe_hbm_read(buf, int(nbytes), int(grid), sink, stream)
+    if rc != 0:
+        raise RuntimeError("conv_probe_hbm_read failed: hipError %d" % rc)

@@ -30,6 +30,23 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_what_its_header_declares():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER.replace("convfwd.h", "convprobe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(conv_probe_\w+)\s*\(", text)))
+    assert declared == sorted(capi.PROBE_EXPORTED)
+    lib = capi.probe_lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert capi.conv_probe_threads() == 256
+    # bad arguments are refused before any launch (hipErrorInvalidValue)
+    with pytest.raises(RuntimeError):
+        capi.conv_probe_mfma(2, 1, 1, 16)
+    with pytest.raises(RuntimeError):
+        capi.conv_probe_mfma(0, 1, 1, None)
+    with pytest.raises(RuntimeError):
+        capi.conv_probe_hbm_read(16, 24, 1, 16)
+
+
 def test_desc_struct_layout_matches_header():
     # int32 ndim, int32 dtype, 4 int64, 5 x int64[3], int32 has_bias, int32 gelu
     assert ctypes.sizeof(capi.conv_fwd_desc_t) == 8 + 4 * 8 + 15 * 8 + 8
