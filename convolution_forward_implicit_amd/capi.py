@@ -30,7 +30,7 @@ EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
             "conv_chain_describe", "conv_chain_out_dims", "conv_chain_useful_flop", "conv_chain_packed_bytes", "conv_chain_pack_weights", "conv_chain_run_packed",
             "conv_chain_run_packed_events", "conv_bwd_data_create", "conv_bwd_data_workspace_bytes",
-            "conv_bwd_data_run", "conv_bwd_data_destroy", "conv_bwd_data_describe", "conv_bwd_weight_create",
+            "conv_bwd_data_run", "conv_bwd_data_run_noalloc", "conv_bwd_data_destroy", "conv_bwd_data_describe", "conv_bwd_weight_create",
             "conv_bwd_weight_workspace_bytes", "conv_bwd_weight_run", "conv_bwd_weight_destroy",
             "conv_bwd_weight_describe"]
 
@@ -117,6 +117,8 @@ def lib():
         L.conv_bwd_data_workspace_bytes.restype = ctypes.c_int
         L.conv_bwd_data_run.argtypes = [P, P, P, P, P, ctypes.c_int64, P]
         L.conv_bwd_data_run.restype = ctypes.c_int
+        L.conv_bwd_data_run_noalloc.argtypes = [P, P, P, P, P]
+        L.conv_bwd_data_run_noalloc.restype = ctypes.c_int
         L.conv_bwd_data_destroy.argtypes = [P]
         L.conv_bwd_data_destroy.restype = None
         L.conv_bwd_data_describe.argtypes = [P]
@@ -273,6 +275,13 @@ def conv_bwd_data_workspace_bytes(plan):
 
 def conv_bwd_data_run(plan, dy, w, dx, workspace, workspace_bytes, stream=0):
     _check(lib().conv_bwd_data_run(plan, dy, w, dx, workspace, int(workspace_bytes), stream))
+
+
+CONV_BWD_DATA_SCRATCH_BYTES = 64 << 20
+
+
+def conv_bwd_data_run_noalloc(plan, dy, w, dx, stream=0):
+    _check(lib().conv_bwd_data_run_noalloc(plan, dy, w, dx, stream))
 
 
 def conv_bwd_data_destroy(plan):

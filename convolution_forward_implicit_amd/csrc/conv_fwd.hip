@@ -19,6 +19,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/convfwd.h"
@@ -520,6 +521,39 @@ bool patch_fits(const TileCfg &c, const conv_fwd_desc_t &d)
     return d.C % c.CC == 0 && ph <= c.PHMAX && pw <= c.PWMAX && d.filt[1] * d.filt[2] <= c.TAPMAX;
 }
 
+}  // namespace
+
+// ---- Backward-data without allocation ---------------------------------------
+// For callers that cannot allocate (graph capture, serving loops): the
+// workspace is this file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never passes the array's name to a kernel -- on
+// the host it is only a stand-in for the symbol -- but the device address
+// hipGetSymbolAddress returns for it, looked up once per device (with that
+// device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[CONV_BWD_DATA_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices];
+
+conv_status_t scratch_of_current_device(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CONV_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CONV_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CONV_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CONV_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -1072,6 +1106,21 @@ conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     return conv_fwd_run(plan->fwd, src, ws, nullptr, dx, stream);
+}
+
+conv_status_t conv_bwd_data_run_noalloc(const conv_bwd_data_plan_t *plan, const void *dy, const void *w, void *dx,
+                                        void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->ws_bytes > (int64_t)CONV_BWD_DATA_SCRATCH_BYTES)
+        return fail(CONV_ERR_UNSUPPORTED,
+                    "backward-data needs %lld bytes of workspace; the allocation-free entry point holds %lld",
+                    (long long)plan->ws_bytes, (long long)CONV_BWD_DATA_SCRATCH_BYTES);
+    if (plan->dx_elems == 0) return conv_bwd_data_run(plan, dy, w, dx, nullptr, 0, stream);
+    void *ws = nullptr;
+    conv_status_t st = scratch_of_current_device(&ws);
+    if (st != CONV_OK) return st;
+    return conv_bwd_data_run(plan, dy, w, dx, ws, (int64_t)CONV_BWD_DATA_SCRATCH_BYTES, stream);
 }
 
 void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan)

@@ -252,6 +252,25 @@ conv_status_t conv_bwd_data_workspace_bytes(const conv_bwd_data_plan_t *plan, in
 conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy, const void *w, void *dx,
                                 void *workspace, int64_t workspace_bytes, void *stream);
 void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan);
+
+/* Backward-data for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * as conv_bwd_data_run, with the workspace taken from a static device array
+ * of CONV_BWD_DATA_SCRATCH_BYTES (64 MiB) that the library holds on each GPU
+ * it runs on until the process ends.  It calls no allocating routine.  The
+ * caller still passes dy, w and dx.
+ *   CONV_ERR_UNSUPPORTED : the plan needs more workspace than the array holds
+ *                          (conv_bwd_data_workspace_bytes > 64 MiB).
+ *   CONV_ERR_HIP         : the array's device address could not be obtained
+ *                          (first call on a device), or a launch failed.
+ *   other errors as conv_bwd_data_run.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, threads or processes sharing the context)
+ * race on it.  Each call writes every workspace byte it reads, so nothing
+ * carries over from the previous call. */
+#define CONV_BWD_DATA_SCRATCH_BYTES (64ll << 20)
+conv_status_t conv_bwd_data_run_noalloc(const conv_bwd_data_plan_t *plan, const void *dy, const void *w, void *dx,
+                                        void *stream);
 const char *conv_bwd_data_describe(const conv_bwd_data_plan_t *plan);
 
 /* ---- Backward-weight (weight gradient) ------------------------------------
