@@ -66,6 +66,51 @@ class ConvFwd:
     def describe(self):
         return capi.conv_fwd_describe(self._plan)
 
+    def packed_bytes(self):
+        """Size of this plan's prepacked weights (ConvError UNSUPPORTED when
+        the plan's kernel reads natural weights only)."""
+        return capi.conv_fwd_packed_bytes(self._plan)
+
+    def pack(self, w, out=None, stream=None):
+        """This plan's prepacked weights (a uint8 cuda tensor) from w,
+        enqueued on `stream`; pack once, reuse for every run_packed."""
+        import torch
+        wp = self._tensor(w, self.w_shape, "w", torch)
+        nbytes = self.packed_bytes()
+        if out is None:
+            out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+        if out.device.type != "cuda" or out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() != nbytes:
+            raise ValueError("packed must be a contiguous cuda uint8 tensor of %d bytes" % nbytes)
+        s = stream if stream is not None else torch.cuda.current_stream(w.device)
+        capi.conv_fwd_pack_weights(self._plan, wp, out.data_ptr(), s.cuda_stream)
+        return out
+
+    def run_packed(self, x, packed, bias=None, out=None, stream=None, events=None):
+        """As __call__, with the weights from pack()."""
+        import torch
+        xp = self._tensor(x, self.x_shape, "x", torch)
+        if packed.device.type != "cuda" or packed.dtype != torch.uint8 or not packed.is_contiguous():
+            raise ValueError("packed must be a contiguous cuda uint8 tensor (from pack)")
+        if packed.numel() != self.packed_bytes():
+            raise ValueError("packed has %d bytes, expected %d" % (packed.numel(), self.packed_bytes()))
+        bp = None
+        if self.has_bias:
+            if bias is None:
+                raise ValueError("this plan has a bias")
+            bp = self._tensor(bias, self.b_shape, "bias", torch)
+        elif bias is not None:
+            raise ValueError("this plan has no bias")
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=x.dtype, device=x.device)
+        yp = self._tensor(out, self.y_shape, "out", torch)
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        if events is None:
+            capi.conv_fwd_run_packed(self._plan, xp, packed.data_ptr(), bp, yp, s.cuda_stream)
+        else:
+            capi.conv_fwd_run_packed_events(self._plan, xp, packed.data_ptr(), bp, yp, s.cuda_stream,
+                                            events[0].cuda_event, events[1].cuda_event)
+        return out
+
     def close(self):
         if getattr(self, "_plan", None):
             capi.conv_fwd_destroy(self._plan)

@@ -26,9 +26,11 @@
 #include "igemm_kernel.h"
 #include "igemm_dma.h"
 #include "patch_kernel.h"
+#include "patch_fixed.h"
 #include "chain_kernel.h"
 #include "chain_packed.h"
 #include "bwd_kernels.h"
+#include "weight_pack.h"
 
 namespace convfwd {
 namespace {
@@ -109,6 +111,31 @@ void launch_patch(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStre
         hipExtLaunchKernelGGL((patch_conv_kernel<TH, TW, BN, CC, NS, PHMAX, PWMAX, TAPMAX, PAD, false, false>), g, b, 0, s, e0, e1, 0, pp);
 }
 
+template <int TH, int TW, int BN, int CC, int NS, int FY, int FX, int DH, int DW, int NW, int PM, int RA, int RR>
+void launch_patchf(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStream_t s, hipEvent_t e0,
+                   hipEvent_t e1)
+{
+    PatchFixedParams pp;
+    pp.k = kp;
+    pp.x_bytes = xb;
+    pp.w_bytes = wb;
+    pp.tiles_h = (kp.Ho + TH - 1) / TH;
+    pp.tiles_w = (kp.Wo + TW - 1) / TW;
+    pp.fd_tw = make_fastdiv(pp.tiles_w);
+    pp.fd_th = make_fastdiv(pp.tiles_h);
+    pp.fd_N = make_fastdiv(kp.N);
+    const dim3 g(grid), b(NW * 64);
+    const bool bias = kp.bias != nullptr;
+    if (bias && kp.gelu)
+        hipExtLaunchKernelGGL((patch_fixed_kernel<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR, true, true>), g, b, 0, s, e0, e1, 0, pp);
+    else if (bias)
+        hipExtLaunchKernelGGL((patch_fixed_kernel<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR, true, false>), g, b, 0, s, e0, e1, 0, pp);
+    else if (kp.gelu)
+        hipExtLaunchKernelGGL((patch_fixed_kernel<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR, false, true>), g, b, 0, s, e0, e1, 0, pp);
+    else
+        hipExtLaunchKernelGGL((patch_fixed_kernel<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR, false, false>), g, b, 0, s, e0, e1, 0, pp);
+}
+
 template <int KT, int TT>
 void launch_wgrad(const WgradParams &wp, int grid, hipStream_t s)
 {
@@ -128,7 +155,7 @@ int wgrad_occupancy()
     return blocks > 0 ? blocks : 1;
 }
 
-enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2 };
+enum { KIND_REG = 0, KIND_DMA = 1, KIND_PATCH = 2, KIND_PATCHF = 3 };
 
 struct TileCfg {
     int dtype;          // conv_dtype_t
@@ -138,8 +165,11 @@ struct TileCfg {
     int lds_bytes;
     launch_fn fn;
     const char *name;
-    int TH, TW, CC, PHMAX, PWMAX, TAPMAX;   // KIND_PATCH only
+    int TH, TW, CC, PHMAX, PWMAX, TAPMAX;   // KIND_PATCH (TH, TW, CC also KIND_PATCHF)
     int KG;             // KIND_DMA: reduction groups per workgroup (0 means 1)
+    int FY, FX, DH, DW; // KIND_PATCHF: the filter's H/W taps and dilation it is compiled for
+    int wimg;           // KIND_PATCHF: bytes of one K-step's prepacked weight image
+    int MF;             // KIND_DMA: MFMA block edge (16 or 32)
 };
 
 #define CFG(DT, BM, BN, BK, WM, WN, VEC)                                                 \
@@ -156,7 +186,7 @@ struct TileCfg {
             &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1, 0>,                            \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB  \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB), \
-            0, 0, 0, 0, 0, 0, 1}
+            0, 0, 0, 0, 0, 0, 1, 0, 0, 0, 0, 0, MF}
 
 // Loads of the next stage issued during the first 1/FL of the products
 #define DMAF(DT, BM, BN, WM, WN, NS, MF, KSUB, FL)                                       \
@@ -165,7 +195,7 @@ struct TileCfg {
             &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 1, FL>,                        \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_f" #FL \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_f" #FL), \
-            0, 0, 0, 0, 0, 0, 1}
+            0, 0, 0, 0, 0, 0, 1, 0, 0, 0, 0, 0, MF}
 
 // Two reduction groups per workgroup (twice the waves, half the K-steps each)
 #define DMA2(DT, BM, BN, WM, WN, NS, MF, KSUB)                                           \
@@ -174,7 +204,7 @@ struct TileCfg {
             &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, 2, 0>,                            \
             (DT ? "bf16_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2" \
                 : "f32_dma_" #BM "x" #BN "_w" #WM "x" #WN "_s" #NS "_m" #MF "_k" #KSUB "_g2"), \
-            0, 0, 0, 0, 0, 0, 2}
+            0, 0, 0, 0, 0, 0, 2, 0, 0, 0, 0, 0, MF}
 
 // Four one-wave reduction groups per workgroup (a quarter of the K-steps each)
 #define DMA4(DT, BM, BN, NS, MF, KSUB)                                                   \
@@ -183,7 +213,7 @@ struct TileCfg {
             &launch_dma<DT, BM, BN, 1, 1, NS, MF, KSUB, 4, 0>,                           \
             (DT ? "bf16_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4"        \
                 : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4"),       \
-            0, 0, 0, 0, 0, 0, 4}
+            0, 0, 0, 0, 0, 0, 4, 0, 0, 0, 0, 0, MF}
 
 #define DMA4F(DT, BM, BN, NS, MF, KSUB, FL)                                              \
     TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), 1, 1, 16 / (DT ? 2 : 4), NS,  \
@@ -191,7 +221,7 @@ struct TileCfg {
             &launch_dma<DT, BM, BN, 1, 1, NS, MF, KSUB, 4, FL>,                          \
             (DT ? "bf16_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4_f" #FL  \
                 : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4_f" #FL), \
-            0, 0, 0, 0, 0, 0, 4}
+            0, 0, 0, 0, 0, 0, 4, 0, 0, 0, 0, 0, MF}
 
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
@@ -203,10 +233,28 @@ struct TileCfg {
             "bf16_patch_" #TH "x" #TW "x" #BN "_c" #CC "_s" #NS "_p" #PHMAX "x" #PWMAX "_d" #PAD, \
             TH, TW, CC, PHMAX, PWMAX, TAPMAX}
 
+// Input-patch kernel with the filter's H/W shape compiled in (bf16, unit H/W
+// stride): box TH x TW (flattened into 32-pixel blocks), BN output channels,
+// CC channels per K-step, NS stages, an FY x FX filter with H/W dilation
+// DH x DW, NW waves.
+#define PFIX(TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR)                          \
+    TileCfg{1, KIND_PATCHF, TH * TW, BN, CC, NW, 1, 8, NS,                                 \
+            PatchFixedShape<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RR>::LDS_BYTES,    \
+            &launch_patchf<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR>,           \
+            "bf16_pfix_" #TH "x" #TW "x" #BN "_c" #CC "_s" #NS "_f" #FY "x" #FX "_d" #DH "x" #DW "_w" #NW \
+            "_l" #PM "_r" #RA "_rr" #RR, TH, TW, CC, 0, 0, 0, 1, FY, FX, DH, DW,          \
+            PatchFixedShape<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RR>::W_BYTES, 32}
+
 // One candidate table, shared by the selector, forced-config creation and
 // the sweeps.  VEC = 16 bytes of channels per load; the VEC = 1 entries serve
 // channel counts that are not a multiple of the vector.
 const TileCfg kCfgs[] = {
+    PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 4, 1, 1, 1),
+    PFIX(16, 32, 32, 16, 2, 3, 3, 2, 2, 4, 0, 1, 1),
+    PFIX(16, 28, 32, 16, 2, 3, 3, 2, 2, 2, 1, 1, 0),
+    PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
+    PFIX(16, 32, 32, 16, 2, 3, 3, 1, 1, 4, 0, 1, 1),
+    PFIX(8, 32, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PATCH(8, 32, 64, 16, 2, 10, 34, 9, 1),
     PATCH(4, 32, 64, 16, 2, 6, 34, 9, 1),
     PATCH(8, 32, 32, 16, 2, 12, 36, 9, 1),
@@ -255,6 +303,8 @@ const TileCfg kCfgs[] = {
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
     DMA4(0, 48, 48, 2, 16, 1),
     DMA4F(0, 48, 48, 2, 16, 1, 4),
+    DMA4(0, 48, 48, 3, 16, 1),
+    DMA2(0, 48, 96, 1, 2, 3, 16, 1),
     DMA2(0, 48, 96, 1, 2, 2, 16, 2),
     DMA4(0, 32, 32, 2, 16, 1),
     DMA2(1, 128, 64, 2, 2, 2, 32, 1),
@@ -398,6 +448,8 @@ struct conv_fwd_plan {
     bool tuned;      // cfg came from an exact-shape tuning record
     int grid;
     KParams kp;      // pointers filled per run
+    PackParams pk;   // prepacked weights: pointers filled per call
+    int64_t packed_bytes;   // 0: the plan's kernel reads natural weights only
     char text[256];
 };
 
@@ -487,7 +539,7 @@ double cost(const TileCfg &c, const conv_fwd_plan &pl, int cus)
 double tiles_of(const TileCfg &c, const conv_fwd_desc_t &d, const int64_t out[3])
 {
     const double tn = (double)((d.K + c.BN - 1) / c.BN);
-    if (c.kind == KIND_PATCH)
+    if (c.kind == KIND_PATCH || c.kind == KIND_PATCHF)
         return (double)d.N * out[0] * (double)((out[1] + c.TH - 1) / c.TH) *
                (double)((out[2] + c.TW - 1) / c.TW) * tn * (double)d.G;
     const int64_t M = d.N * out[0] * out[1] * out[2];
@@ -496,7 +548,7 @@ double tiles_of(const TileCfg &c, const conv_fwd_desc_t &d, const int64_t out[3]
 
 double steps_of(const TileCfg &c, const conv_fwd_desc_t &d)
 {
-    if (c.kind == KIND_PATCH) return (double)d.filt[0] * (double)(d.C / c.CC);
+    if (c.kind == KIND_PATCH || c.kind == KIND_PATCHF) return (double)d.filt[0] * (double)(d.C / c.CC);
     const int64_t Kred = d.C * d.filt[0] * d.filt[1] * d.filt[2];
     const int64_t kg = c.KG > 1 ? c.KG : 1;
     return (double)(((Kred + c.BK - 1) / c.BK + kg - 1) / kg);   // K-steps of one reduction group
@@ -519,6 +571,13 @@ bool patch_fits(const TileCfg &c, const conv_fwd_desc_t &d)
     const int64_t ph = (c.TH - 1) * d.stride[1] + (d.filt[1] - 1) * d.dilation[1] + 1;
     const int64_t pw = (c.TW - 1) * d.stride[2] + (d.filt[2] - 1) * d.dilation[2] + 1;
     return d.C % c.CC == 0 && ph <= c.PHMAX && pw <= c.PWMAX && d.filt[1] * d.filt[2] <= c.TAPMAX;
+}
+
+// The fixed-filter patch kernel: unit H/W stride and exactly its filter.
+bool patchf_fits(const TileCfg &c, const conv_fwd_desc_t &d)
+{
+    return d.C % c.CC == 0 && d.filt[0] <= 32 && d.stride[1] == 1 && d.stride[2] == 1 && d.filt[1] == c.FY && d.filt[2] == c.FX &&
+           d.dilation[1] == c.DH && d.dilation[2] == c.DW;
 }
 
 }  // namespace
@@ -600,6 +659,7 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         if (c.dtype != d.dtype) return false;
         if (c.kind == KIND_REG) return c.VEC == want_vec;
         if (c.kind == KIND_DMA) return dma_ok;
+        if (c.kind == KIND_PATCHF) return dma_ok && patchf_fits(c, d);
         return dma_ok && patch_fits(c, d);
     };
     if (forced >= 0) {
@@ -615,8 +675,10 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         if (c.VEC != 1 && !eligible(c)) {
             delete pl;
             return fail(CONV_ERR_UNSUPPORTED, "config %s needs C %% %d == 0 (C = %lld)%s", c.name,
-                        c.kind == KIND_PATCH ? c.CC : c.VEC, (long long)d.C,
+                        c.kind == KIND_PATCH || c.kind == KIND_PATCHF ? c.CC : c.VEC, (long long)d.C,
                         c.kind == KIND_PATCH ? ", x and w below 2 GiB, and a patch / tap count within its limits"
+                        : c.kind == KIND_PATCHF ? ", x and w below 2 GiB, unit H/W stride and exactly its H/W filter "
+                                                  "and dilation"
                         : c.kind == KIND_DMA ? " and x, w below 2 GiB" : "");
         }
         pl->cfg = forced;
@@ -661,13 +723,37 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     kp.fd_Y = make_fastdiv(kp.Y);
     kp.fd_tn = make_fastdiv(kp.tiles_n);
     kp.fd_tm = make_fastdiv(kp.tiles_m);
+    // prepacked weight image of this plan's kernel (none for the register-staged one)
+    PackParams &pk = pl->pk;
+    pk.esz = pl->esz;
+    pk.K = kp.K; pk.Kred = kp.Kred; pk.C = kp.C; pk.Z = kp.Z; pk.taps = kp.Y * kp.X;
+    pk.BN = c.BN; pk.tiles_n = kp.tiles_n;
+    double img = 0.0;
+    if (c.kind == KIND_DMA) {
+        pk.mode = 0;
+        pk.subk = 128 / pl->esz;
+        pk.ksub = c.BK / pk.subk;
+        pk.vec = 16 / pl->esz;
+        pk.nk = (kp.Kred + c.BK - 1) / c.BK;
+        pk.sw4 = (c.MF == 32 && kp.C % (2 * pk.vec) == 0) ? 1 : 0;
+        img = (double)d.G * kp.tiles_n * pk.nk * pk.ksub * c.BN * 128.0;
+    } else if (c.kind == KIND_PATCHF) {
+        pk.mode = 1;
+        pk.ncs = kp.C / c.CC;
+        pk.cc = c.CC;
+        pk.wslots = (c.CC / 8) * pk.taps * c.BN;
+        pk.img_slots = c.wimg / 16;
+        img = (double)d.G * kp.tiles_n * kp.Z * pk.ncs * (double)c.wimg;
+    }
+    pl->packed_bytes = img < 2147483647.0 ? (int64_t)img : 0;
+    pk.slots = pl->packed_bytes / 16;
     const double grid = tiles_of(c, d, out);
     if (grid >= 2147483647.0) {
         delete pl;
         return fail(CONV_ERR_UNSUPPORTED, "grid too large");
     }
     pl->grid = (int)grid;
-    if (c.kind == KIND_PATCH)
+    if (c.kind == KIND_PATCH || c.kind == KIND_PATCHF)
         snprintf(pl->text, sizeof(pl->text),
                  "patch %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%d boxes/plane, %d n-tiles) lds=%dB%s", c.name,
                  kp.M, kp.K, kp.Kred, kp.G, pl->grid, (kp.Ho + c.TH - 1) / c.TH, (kp.Wo + c.TW - 1) / c.TW,
@@ -719,9 +805,66 @@ static bool overlaps(const void *a, int64_t an, const void *b, int64_t bn)
     return pa < pb + bn && pb < pa + an;
 }
 
+static conv_status_t run_impl(const conv_fwd_plan_t *plan, const void *x, const void *w, const void *bias, void *y,
+                              void *stream, void *start_event, void *stop_event, bool packed);
+
 conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, const void *w,
                                   const void *bias, void *y, void *stream, void *start_event,
                                   void *stop_event)
+{
+    return run_impl(plan, x, w, bias, y, stream, start_event, stop_event, false);
+}
+
+conv_status_t conv_fwd_packed_bytes(const conv_fwd_plan_t *plan, int64_t *bytes)
+{
+    if (!plan || !bytes) return fail(CONV_ERR_INVALID_ARG, "plan or bytes is NULL");
+    if (plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
+                    kCfgs[plan->cfg].name);
+    *bytes = plan->packed_bytes;
+    return CONV_OK;
+}
+
+conv_status_t conv_fwd_pack_weights(const conv_fwd_plan_t *plan, const void *w, void *packed, void *stream)
+{
+    if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
+                    kCfgs[plan->cfg].name);
+    if (!w || !packed) return fail(CONV_ERR_INVALID_ARG, "w or packed is NULL");
+    if (((uintptr_t)w | (uintptr_t)packed) & 15u)
+        return fail(CONV_ERR_INVALID_ARG, "w and packed must be 16-byte aligned");
+    if (overlaps(packed, plan->packed_bytes, w, plan->w_elems * plan->esz))
+        return fail(CONV_ERR_INVALID_ARG, "packed overlaps w");
+    PackParams pk = plan->pk;
+    pk.w = w;
+    pk.out = packed;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((pk.slots + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)stream, pk);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    return CONV_OK;
+}
+
+conv_status_t conv_fwd_run_packed_events(const conv_fwd_plan_t *plan, const void *x, const void *packed,
+                                         const void *bias, void *y, void *stream, void *start_event,
+                                         void *stop_event)
+{
+    if (plan && plan->packed_bytes == 0)
+        return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
+                    kCfgs[plan->cfg].name);
+    return run_impl(plan, x, packed, bias, y, stream, start_event, stop_event, true);
+}
+
+conv_status_t conv_fwd_run_packed(const conv_fwd_plan_t *plan, const void *x, const void *packed,
+                                  const void *bias, void *y, void *stream)
+{
+    return conv_fwd_run_packed_events(plan, x, packed, bias, y, stream, nullptr, nullptr);
+}
+
+static conv_status_t run_impl(const conv_fwd_plan_t *plan, const void *x, const void *w, const void *bias, void *y,
+                              void *stream, void *start_event, void *stop_event, bool packed)
 {
     if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
     const conv_fwd_desc_t &d = plan->desc;
@@ -735,14 +878,16 @@ conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, co
     if (bias && ((uintptr_t)bias & (uintptr_t)(plan->esz - 1)))
         return fail(CONV_ERR_INVALID_ARG, "bias is not aligned to its element size");
     const int64_t e = plan->esz;
-    if (overlaps(y, plan->y_elems * e, x, plan->x_elems * e) || overlaps(y, plan->y_elems * e, w, plan->w_elems * e) ||
+    const int64_t wbytes = packed ? plan->packed_bytes : plan->w_elems * e;
+    if (overlaps(y, plan->y_elems * e, x, plan->x_elems * e) || overlaps(y, plan->y_elems * e, w, wbytes) ||
         overlaps(y, plan->y_elems * e, bias, plan->b_elems * e))
         return fail(CONV_ERR_INVALID_ARG, "y overlaps an input");
     KParams kp = plan->kp;
     kp.x = x; kp.w = w; kp.bias = bias; kp.y = y;
+    kp.wpacked = packed ? 1 : 0;
     (void)d;
     (void)hipGetLastError();  // clear a stale error so the check below is ours
-    kCfgs[plan->cfg].fn(kp, (uint32_t)(plan->x_elems * e), (uint32_t)(plan->w_elems * e), plan->grid,
+    kCfgs[plan->cfg].fn(kp, (uint32_t)(plan->x_elems * e), (uint32_t)wbytes, plan->grid,
                         (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));

@@ -255,16 +255,25 @@ igemm_dma_kernel(DmaParams dp)
             }
         }
     }
+    // K-steps of this group: kstart .. kstart + nkh - 1
+    const int nk = (p.Kred + S::BK - 1) / S::BK;
+    // Weight rows: GKZYXC rows of the tile's channels, or (prepacked) the
+    // lane's 16-byte slot of a K-step's image -- the B part of the LDS stage
+    // exactly as this kernel lays it out (swizzle included, zeros for
+    // channels past K and reduction past Kred), KSUB sub-slices of BN*128
+    // bytes per step, steps of one (group, channel tile) contiguous.
+    constexpr int STEP_B = KSUB * BN * 128;
     uint32_t b_off[S::B_PER_W];
 #pragma unroll
     for (int t = 0; t < S::B_PER_W; ++t) {
         const int n = n0 + (wave * S::B_PER_W + t) * 8 + lrow;
         const int cht = chunk ^ (sw4 & ((wave * S::B_PER_W + t) >> 1));   // row bit 4 = block bit 1
-        b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + cht * S::VEC) * S::ESZ) : kOutOfRange;
+        if (p.wpacked)
+            b_off[t] = (uint32_t)(((g * p.tiles_n + n_tile) * nk) * STEP_B + (wave * S::B_PER_W + t) * 1024 + lane * 16);
+        else
+            b_off[t] = n < p.K ? (uint32_t)(((g * p.K + n) * p.Kred + cht * S::VEC) * S::ESZ) : kOutOfRange;
     }
 
-    // K-steps of this group: kstart .. kstart + nkh - 1
-    const int nk = (p.Kred + S::BK - 1) / S::BK;
     const int nkh = (nk + KG - 1) / KG;
     const int kstart = kg * nkh;
 
@@ -325,7 +334,8 @@ igemm_dma_kernel(DmaParams dp)
                                 (unsigned)(a_bw[t] + ts.xw) < (unsigned)p.Wi;
                 dv[u][t] = ok ? (uint32_t)(a_base[t] + ts.offb) : kOutOfRange;
             }
-            const uint32_t kb = (uint32_t)((k0 + u * S::SUBK) * S::ESZ);
+            const uint32_t kb = p.wpacked ? (uint32_t)((k0 / S::BK) * STEP_B + u * BN * 128)
+                                          : (uint32_t)((k0 + u * S::SUBK) * S::ESZ);
 #pragma unroll
             for (int t = 0; t < S::B_PER_W; ++t)
                 dv[u][S::A_PER_W + t] = (rok && b_off[t] != kOutOfRange) ? b_off[t] + kb : kOutOfRange;

@@ -65,6 +65,8 @@ struct KParams {
     int tiles_n;        // ceil(K / BN)
     int gelu;
     int out_vec;        // K % (16 / sizeof(out)) == 0: whole-vector stores
+    int wpacked;        // w is the plan's prepacked weight image (direct-to-LDS and
+                        // fixed-filter patch kernels), not GKZYXC
     FastDiv fd_Wo, fd_Ho, fd_Do, fd_C, fd_X, fd_Y;
     FastDiv fd_tn, fd_tm;   // tiles_n, tiles_m
 };

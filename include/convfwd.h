@@ -130,6 +130,35 @@ conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, co
                                   const void *bias, void *y, void *stream,
                                   void *start_event, void *stop_event);
 
+/* ---- Prepacked weights ----------------------------------------------------
+ * The ExecuTorch conv1d issue's conv2d path (section "The conv2d path
+ * already solves this") prepacks its weights once, ahead of the runs.  The
+ * packed form of a plan's weights is the weight part of every LDS stage of
+ * the plan's kernel, in the order the kernel consumes it: one image per
+ * (group, output-channel tile, K-step), zeros wherever the kernel would
+ * load nothing.  Each K-step then fetches its weights as contiguous
+ * kilobytes.  It depends on the plan (its tile configuration), not only on
+ * the problem: pack with the plan that runs.  Same results as conv_fwd_run
+ * for the same weights, bit for bit (same kernel, same summation order).
+ *
+ * conv_fwd_packed_bytes: size of the packed weights (a multiple of 16).
+ *   CONV_ERR_UNSUPPORTED if the plan's kernel reads natural weights only
+ *   (the register-staged and the runtime-filter patch kernels), or the image
+ *   would reach 2 GiB; INVALID_ARG for NULL arguments.
+ * conv_fwd_pack_weights: enqueues the rearrangement of w (GKZYXC, the
+ *   plan's dtype) into `packed`, a caller-owned device buffer of
+ *   conv_fwd_packed_bytes bytes, on `stream`.  Both 16-byte aligned, not
+ *   overlapping.  Allocates nothing.
+ * conv_fwd_run_packed(_events): as conv_fwd_run(_events) with the packed
+ *   weights in place of w (16-byte aligned; y must not overlap it). */
+conv_status_t conv_fwd_packed_bytes(const conv_fwd_plan_t *plan, int64_t *bytes);
+conv_status_t conv_fwd_pack_weights(const conv_fwd_plan_t *plan, const void *w, void *packed, void *stream);
+conv_status_t conv_fwd_run_packed(const conv_fwd_plan_t *plan, const void *x, const void *packed,
+                                  const void *bias, void *y, void *stream);
+conv_status_t conv_fwd_run_packed_events(const conv_fwd_plan_t *plan, const void *x, const void *packed,
+                                         const void *bias, void *y, void *stream, void *start_event,
+                                         void *stop_event);
+
 /* Frees a plan.  NULL is a no-op. */
 void conv_fwd_destroy(conv_fwd_plan_t *plan);
 

@@ -21,10 +21,13 @@ extern "C" {
 int32_t conv_probe_threads(void);
 
 /* Back-to-back MFMA work: kind 0 = v_mfma_f32_32x32x16_bf16, kind 1 =
- * v_mfma_f32_16x16x4_f32, `iters` rounds of independent accumulator chains
- * per wave, `grid` workgroups.  sink: device buffer of grid * 256 floats
- * (each lane writes its accumulator sum).  *flop (may be NULL) receives the
- * useful work the launch performs (2*M*N*K per instruction). */
+ * v_mfma_f32_16x16x4_f32, kind 2 = v_mfma_f32_16x16x32_bf16, `iters` rounds
+ * of independent accumulator chains per wave, `grid` workgroups.  sink:
+ * device buffer of grid * 256 floats (each lane writes its accumulator
+ * sum).  *flop (may be NULL) receives the useful work the launch performs
+ * (2*M*N*K per instruction).  kind 3 is an LDS read-rate probe instead
+ * (16-byte conflict-free reads, eight in flight per wave); *flop then
+ * receives the bytes it reads from LDS. */
 int32_t conv_probe_mfma(int32_t kind, int32_t iters, int32_t grid, void *sink, void *stream, double *flop);
 
 /* Streaming read of `bytes` (a multiple of 16, >= 16) from device buffer

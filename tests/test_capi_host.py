@@ -40,7 +40,7 @@ def test_probe_library_exports_what_its_header_declares():
     assert capi.conv_probe_threads() == 256
     # bad arguments are refused before any launch (hipErrorInvalidValue)
     with pytest.raises(RuntimeError):
-        capi.conv_probe_mfma(2, 1, 1, 16)
+        capi.conv_probe_mfma(4, 1, 1, 16)
     with pytest.raises(RuntimeError):
         capi.conv_probe_mfma(0, 1, 1, None)
     with pytest.raises(RuntimeError):
@@ -178,12 +178,24 @@ def test_forced_config_dtype_and_vector_rules():
                 capi.conv_fwd_create_with_config(d_bf16, i)
             assert e.value.status == capi.CONV_ERR_UNSUPPORTED
             continue
-        plan = capi.conv_fwd_create_with_config(d_bf16, i)
+        m = re.search(r"_pfix_.*_f(\d+)x(\d+)_d(\d+)x(\d+)", name)
+        d_ok, d_bad = d_bf16, d_odd
+        if m:   # fixed-filter patch kernels: exactly their own H/W filter and dilation
+            FY, FX, DH, DW = (int(v) for v in m.groups())
+            fit = sd.problem(1, 1, 32, 16, (1, 6 + DH * (FY - 1), 6 + DW * (FX - 1)), (1, FY, FX), pad=(0, 1, 1),
+                             dil=(1, DH, DW))
+            d_ok = desc_from_problem(fit, "bf16")
+            d_bad = desc_from_problem(dict(fit, C=5), "bf16")
+            other = desc_from_problem(dict(fit, dil=(1, DH + 1, DW)), "bf16")
+            with pytest.raises(ConvError) as e:
+                capi.conv_fwd_create_with_config(other, i)
+            assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+        plan = capi.conv_fwd_create_with_config(d_ok, i)
         assert name in capi.conv_fwd_describe(plan)
         capi.conv_fwd_destroy(plan)
         if not name.endswith("_v1"):   # 16-byte channel vectors / slices need C % 8 (16, 32) == 0
             with pytest.raises(ConvError):
-                capi.conv_fwd_create_with_config(d_odd, i)
+                capi.conv_fwd_create_with_config(d_bad, i)
     with pytest.raises(ConvError):
         capi.conv_fwd_create_with_config(d_bf16, n)
     with pytest.raises(ConvError):
@@ -245,7 +257,7 @@ def test_selector_coefficients_match_compiled_configs():
     names = {line.split('"')[1] for line in open(inc) if line.strip().startswith('{"')}
     compiled = {capi.conv_fwd_config_name(i) for i in range(capi.conv_fwd_num_configs())}
     assert names and names <= compiled, names - compiled
-    dma = {n for n in compiled if "_dma_" in n or "_patch_" in n}
+    dma = {n for n in compiled if "_dma_" in n or "_patch_" in n or "_pfix_" in n}
     assert dma <= names, dma - names
 
 
@@ -352,6 +364,59 @@ def test_useful_flop_comes_from_the_library(wid):
     assert round(total / 1e9, 3) == {1: 0.553, 2: 1.880, 3: 60.162, 4: 7.399, 5: 11.098}[wid]
     with pytest.raises(ConvError):
         capi.conv_fwd_useful_flop(None)
+
+
+def _cfg_index(pattern):
+    import re as _re
+    return next(i for i in range(capi.conv_fwd_num_configs()) if _re.search(pattern, capi.conv_fwd_config_name(i)))
+
+
+def test_packed_bytes_sizes_and_refusals():
+    """conv_fwd_packed_bytes: the direct-to-LDS image is one BN x 128-byte
+    block per sub-slice and K-step of every (group, channel tile); the
+    fixed-filter patch image one W_BYTES image per (group, channel tile,
+    depth tap, channel slice); the register-staged kernel has none."""
+    p = sd.problem(2, 2, 32, 40, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1))
+    d = desc_from_problem(p, "bf16")
+    i = _cfg_index(r"^bf16_dma_128x64_w2x2_s2_m32_k1$")
+    plan = capi.conv_fwd_create_with_config(d, i)
+    try:
+        nk = -(-(32 * 9) // 64)
+        assert capi.conv_fwd_packed_bytes(plan) == 2 * 1 * nk * 1 * 64 * 128
+    finally:
+        capi.conv_fwd_destroy(plan)
+    i = _cfg_index(r"^bf16_\d+x\d+x\d+_w\dx\d_v8$")
+    plan = capi.conv_fwd_create_with_config(d, i)
+    try:
+        with pytest.raises(ConvError) as e:
+            capi.conv_fwd_packed_bytes(plan)
+        assert e.value.status == capi.CONV_ERR_UNSUPPORTED
+        with pytest.raises(ConvError):
+            capi.conv_fwd_pack_weights(plan, 16, 4096, 0)
+        with pytest.raises(ConvError):
+            capi.conv_fwd_run_packed(plan, 16, 4096, None, 8192, 0)
+    finally:
+        capi.conv_fwd_destroy(plan)
+    with pytest.raises(ConvError):
+        capi.conv_fwd_packed_bytes(None)
+
+
+def test_pack_and_run_packed_refuse_bad_arguments_before_launching():
+    p = sd.conv1d_problem(2, 64, 64, 100, 3, 1, 1)
+    plan = capi.conv_fwd_create_with_config(desc_from_problem(p, "bf16"), _cfg_index(r"^bf16_dma_128x64_w2x2_s2_m32_k1$"))
+    try:
+        with pytest.raises(ConvError):
+            capi.conv_fwd_pack_weights(plan, None, 4096, 0)          # w NULL
+        with pytest.raises(ConvError):
+            capi.conv_fwd_pack_weights(plan, 8, 4096, 0)             # misaligned
+        with pytest.raises(ConvError):
+            capi.conv_fwd_pack_weights(plan, 4096, 4096, 0)          # overlap
+        with pytest.raises(ConvError):
+            capi.conv_fwd_run_packed(plan, 16, None, None, 4096, 0)  # packed NULL
+        with pytest.raises(ConvError):
+            capi.conv_fwd_run_packed(plan, 8, 16, None, 4096, 0)     # misaligned x
+    finally:
+        capi.conv_fwd_destroy(plan)
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -124,8 +124,20 @@ def _configs():
 CONFIGS = _configs()
 
 
+def _pfix_filter(name):
+    """(FY, FX, DH, DW) a fixed-filter patch configuration is compiled for
+    (its name carries _f<FY>x<FX>_d<DH>x<DW>), or None for other kinds."""
+    m = re.search(r"_pfix_.*_f(\d+)x(\d+)_d(\d+)x(\d+)", name)
+    return tuple(int(v) for v in m.groups()) if m else None
+
+
 def _ragged_problem(name):
     # 2-D, 13 x 11 outputs (ragged against every tile and box), K = 40, G = 2
+    pf = _pfix_filter(name)
+    if pf:
+        FY, FX, DH, DW = pf    # the filter the configuration is compiled for; 13 x 11 outputs
+        return sd.problem(2, 2, 32, 40, (1, 13 + (FY - 1) * DH - 2, 11 + (FX - 1) * DW - 2), (1, FY, FX),
+                          (1, 1, 1), (0, 1, 1), (1, DH, DW))
     if "_patch_" in name:
         C = 32        # a multiple of every patch kernel's channel slice
     else:
@@ -197,10 +209,113 @@ def test_dma_configs_whole_subslice_channels(dev, cfg, name):
         assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
 
 
+PACKABLE = [(i, n) for i, n in CONFIGS if "_dma_" in n or "_pfix_" in n]
+
+
+def run_packed(dev, p, dtype, x, w, b, gelu, config=None):
+    """The plan's prepacked weights (conv_fwd_pack_weights), then
+    conv_fwd_run_packed; also returns the plan."""
+    from convolution_forward_implicit_amd import ConvFwd
+    c = ConvFwd(p, dtype, b is not None, gelu, config=config)
+    print("case: packed", p, dtype, "gelu" if gelu else "", c.describe(), flush=True)
+    wt = to_dev(w, dtype, dev)
+    pk = c.pack(wt)
+    y = c.run_packed(to_dev(x, dtype, dev), pk, None if b is None else to_dev(b, dtype, dev))
+    torch.cuda.synchronize()
+    return y, c
+
+
+def same_bits(a, b):
+    view = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return torch.equal(a.view(view), b.view(view))
+
+
+@pytest.mark.parametrize("cfg,name", PACKABLE, ids=[n for _, n in PACKABLE])
+def test_every_packable_config_prepacked_weights(dev, cfg, name):
+    """Prepacked weights (f-3): on the ragged problem (several channel
+    tiles, a ragged reduction), with bias + GELU, the packed run is bit for
+    bit the natural run (same kernel, same order), and with integer inputs
+    bit-exact against the oracle."""
+    dt = "bf16" if name.startswith("bf16") else "f32"
+    p = _ragged_problem(name)
+    x, w, b = sd.random_inputs(p, dt, 37, True)
+    yn, c = run(dev, p, dt, x, w, b, True, config=cfg)
+    yp, _ = run_packed(dev, p, dt, x, w, b, True, config=cfg)
+    assert same_bits(yn, yp)
+    xi, wi, bi = sd.random_inputs(p, dt, 38, True, kind="int")
+    y, _ = run_packed(dev, p, dt, xi, wi, bi, False, config=cfg)
+    r = ref.conv_fwd(p, xi, wi, bi, False, want_absdot=False)
+    if dt == "f32":
+        assert np.array_equal(host(y), r)
+    else:
+        assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
+
+
+def _packed_plan_for(wid, li):
+    """The tile configuration the prepacked path runs a workload layer with:
+    the selector's, when it has a packed form."""
+    from convolution_forward_implicit_amd import ConvFwd, ConvError
+    p, hb, ge = sd.layers(wid)[li]
+    c = ConvFwd(p, sd.dtype_of(wid), hb, ge)
+    try:
+        c.packed_bytes()
+    except ConvError:
+        return None
+    return c
+
+
+@pytest.mark.parametrize("wid", [1, 2, 4, 5])
+def test_workload_prepacked_weights(dev, wid):
+    """The workloads at full size with prepacked weights in the plan the
+    benchmark times: every output bit for bit the natural run, and against
+    the oracle at the per-element bound."""
+    W = sd.workload(wid)
+    dt = W["dtype"]
+    x = W["x"]
+    for li, (p, hb, ge) in enumerate(W["layers"]):
+        if _packed_plan_for(wid, li) is None:
+            pytest.skip("the selector's kernel for this layer reads natural weights only")
+        yn, _ = run(dev, p, dt, x, W["w"][li], W["b"][li], ge)
+        yp, c = run_packed(dev, p, dt, x, W["w"][li], W["b"][li], ge)
+        assert same_bits(yn, yp)
+        assert_close(host(yp), p, dt, x, W["w"][li], W["b"][li], ge)
+        x = host(yp).astype(np.float32)
+
+
+@pytest.mark.parametrize("name_re", [r"_dma_", r"_pfix_"])
+def test_prepacked_image_holds_every_weight_chunk(dev, name_re):
+    """The packed image is a rearrangement of w with zero padding: every
+    nonzero 16-byte chunk of w appears in it as often as in w times the
+    number of times the kernel loads it (once per K-step image), and
+    conv_fwd_packed_bytes is its size."""
+    from convolution_forward_implicit_amd import ConvFwd
+    cfg, name = next((i, n) for i, n in PACKABLE if re.search(name_re, n) and n.startswith("bf16"))
+    p = _ragged_problem(name)
+    _, w, _ = sd.random_inputs(p, "bf16", 39, False)
+    c = ConvFwd(p, "bf16", config=cfg)
+    wt = to_dev(w, "bf16", dev)
+    pk = c.pack(wt)
+    torch.cuda.synchronize()
+    assert pk.numel() == c.packed_bytes() and pk.numel() % 16 == 0
+    chunks = pk.cpu().numpy().view(np.uint16).reshape(-1, 8)
+    nat = bits(wt).reshape(-1, 8)
+    key = lambda a: np.ascontiguousarray(a).view(np.dtype((np.void, 16))).ravel()
+    got = key(chunks[(chunks != 0).any(axis=1)])
+    want = key(nat[(nat != 0).any(axis=1)])
+    # every weight chunk is in exactly one K-step image (each K-step loads a
+    # distinct slice of the reduction for a distinct channel tile)
+    assert np.array_equal(np.sort(got), np.sort(want))
+
+
 @pytest.mark.parametrize("cfg,name", CONFIGS, ids=[n for _, n in CONFIGS])
 def test_every_config_3d_strided_dilated(dev, cfg, name):
     dt = "bf16" if name.startswith("bf16") else "f32"
-    if "_patch_" in name:
+    pf = _pfix_filter(name)
+    if pf:
+        # any depth stride/dilation/padding; in H and W the compiled filter at unit stride
+        FY, FX, DH, DW = pf
+        p = sd.problem(2, 2, 32, 40, (5, 10, 37), (3, FY, FX), (2, 1, 1), (2, 1, 2), (2, DH, DW))
+    elif "_patch_" in name:
         # the patch kernels take any depth stride/dilation/padding; in H and W
         # a 3x3 filter at unit stride fits every configuration's patch
         p = sd.problem(2, 2, 32, 40, (5, 10, 37), (3, 3, 3), (2, 1, 1), (2, 1, 1), (2, 1, 1))
@@ -229,7 +344,7 @@ def test_every_config_gelu_range(dev, cfg, name):
         x = sd.round_bf16(x)
     w = np.zeros(ws, dtype=np.float32)
     for k in range(p["K"]):
-        w[:, k, 0, 1, 1, k % p["C"]] = 1.0
+        w[:, k, 0, p["filt"][1] // 2, p["filt"][2] // 2, k % p["C"]] = 1.0
     y, _ = run(dev, p, dt, x, w, None, True, config=cfg)
     assert_close(host(y), p, dt, x, w, None, True)
 
