@@ -196,7 +196,19 @@ class Runner:
         if self.fused == "prepacked":
             # weights are constant across steps: prepack once per set, as a model load would
             st["wp"] = self.chain.pack(st["w1"], st["w2"], stream=self.stream)
+        elif not self.fused:
+            # each layer's weights in its plan's prepacked form, where the plan's kernel has one
+            from convolution_forward_implicit_amd import ConvError
+            st["wp"] = []
+            for li, c in enumerate(self.convs):
+                try:
+                    st["wp"].append(c.pack(st["w"][li], stream=self.stream))
+                except ConvError:
+                    st["wp"].append(None)
         return st
+
+    def packable(self):
+        return (not self.fused) and any(v is not None for v in self.sets[0]["wp"])
 
     def set_bytes(self, st):
         tot = 0
@@ -226,8 +238,9 @@ class Runner:
         torch.cuda.synchronize()
         return nsets, sb
 
-    def step(self, st, evs=None):
-        """evs: None, or one (start, stop) event pair per kernel."""
+    def step(self, st, evs=None, packed=False):
+        """evs: None, or one (start, stop) event pair per kernel; packed: run
+        the layers that have prepacked weights from them."""
         s = self.stream
         if self.fused == "prepacked":
             self.chain.run_packed(st["x"], st["wp"], st["b1"], st["b2"], out=st["y"], stream=s,
@@ -238,7 +251,11 @@ class Runner:
         else:
             x = st["x"]
             for li, c in enumerate(self.convs):
-                c(x, st["w"][li], st["b"][li], out=st["outs"][li], stream=s, events=evs[li] if evs else None)
+                ev = evs[li] if evs else None
+                if packed and st["wp"][li] is not None:
+                    c.run_packed(x, st["wp"][li], st["b"][li], out=st["outs"][li], stream=s, events=ev)
+                else:
+                    c(x, st["w"][li], st["b"][li], out=st["outs"][li], stream=s, events=ev)
                 x = st["outs"][li]
 
     def outputs(self, st):
@@ -261,7 +278,7 @@ def timed_steps(r, K, pick):
     return start.elapsed_time(end) / K, time.perf_counter() - t0
 
 
-def kernel_pass(r, L, pick):
+def kernel_pass(r, L, pick, packed=False):
     """L steps, each kernel recording start/stop events from inside its own
     launch: per-kernel durations in microseconds, [kernel][launch]."""
     import torch
@@ -275,7 +292,7 @@ def kernel_pass(r, L, pick):
             b.record(r.stream)
     torch.cuda.synchronize()
     for i in range(L):
-        r.step(r.sets[pick(i)], ev[i])
+        r.step(r.sets[pick(i)], ev[i], packed)
     torch.cuda.synchronize()
     return np.array([[ev[i][k][0].elapsed_time(ev[i][k][1]) * 1e3 for i in range(L)] for k in range(nk)])
 
@@ -313,6 +330,20 @@ def measure(r, steps, warmup, launches, workload):
     us = kernel_pass(r, launches, lambda i: (i + 1) % nsets)
     total = float(sum(r.flops))
     layers = [layer_record(r, k, us[k], workload) for k in range(len(r.kernels))]
+    if r.packable():
+        # the same layers run from their plan-time prepacked weights (A/B)
+        usp = kernel_pass(r, launches, lambda i: (i + 1) % nsets, packed=True)
+        for k, lay in enumerate(layers):
+            if r.sets[0]["wp"][k] is None:
+                lay["prepacked"] = None
+                continue
+            med = float(np.median(usp[k]))
+            ach = r.flops[k] / (med * 1e-6) / 1e12
+            lay["prepacked"] = {"us_median": round(med, 3), "us_mean": round(float(np.mean(usp[k])), 3),
+                                "tflops": round(ach, 2), "frac_of_mfma_peak": round(ach / PEAK_TFLOPS[r.dt], 4),
+                                "bytes": int(r.sets[0]["wp"][k].numel())}
+            if "target" in lay:
+                lay["target"]["met_prepacked"] = med <= lay["target"]["us_at_most"]
     rec = {"dtype": r.dt, "batch": r.W["layers"][0][0]["N"], "useful_gflop_per_step": round(total / 1e9, 4),
            "step_tflops_cold": round(total / (ms_cold * 1e-3) / 1e12, 3), "ms_per_step_cold": round(ms_cold, 5),
            "step_tflops_warm": round(total / (ms_warm * 1e-3) / 1e12, 3), "ms_per_step_warm": round(ms_warm, 5),

@@ -33,7 +33,8 @@ def problem(N, G, C, K, inp, filt, stride, pad, dil):
 def grid():
     """The calibration grid: audio-style 1-D convs (the Whisper frontend
     shapes and neighbours), plain and grouped 2-D convs, grouped 3-D convs
-    with and without dilation."""
+    with and without dilation (enough dilation-2 shapes that every
+    fixed-filter configuration compiled for it gets calibrated)."""
     out = []
     for N, C, K, L, k, s in [(1, 80, 384, 3000, 3, 1), (1, 384, 384, 3000, 3, 2), (4, 80, 384, 3000, 3, 1),
                              (32, 80, 384, 3000, 3, 1), (32, 384, 384, 3000, 3, 2), (8, 256, 256, 1000, 3, 1),
@@ -49,7 +50,9 @@ def grid():
         out.append(problem(N, G, C, K, (1, H, H), (1, k, k), (1, s, s), (0, p, p), (1, d, d)))
     for N, G, C, K, D, H, k, p, d in [(2, 8, 32, 32, 16, 28, 3, 2, 2), (2, 1, 64, 64, 16, 28, 3, 1, 1),
                                       (1, 4, 32, 32, 8, 56, 3, 1, 1), (4, 1, 32, 64, 8, 28, 3, 1, 1),
-                                      (2, 16, 16, 16, 16, 28, 3, 1, 1), (1, 2, 64, 64, 32, 32, 3, 1, 1)]:
+                                      (2, 16, 16, 16, 16, 28, 3, 1, 1), (1, 2, 64, 64, 32, 32, 3, 1, 1),
+                                      (1, 8, 32, 32, 16, 28, 3, 2, 2), (4, 8, 32, 32, 8, 28, 3, 2, 2),
+                                      (2, 4, 32, 32, 16, 32, 3, 2, 2), (2, 16, 32, 32, 8, 28, 3, 2, 2)]:
         out.append(problem(N, G, C, K, (D, H, H), (k, k, k), (1, 1, 1), (p, p, p), (d, d, d)))
     return out
 

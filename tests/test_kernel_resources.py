@@ -2,7 +2,7 @@
 representative instantiations of every code path (wide-N tiles, four and
 two reduction groups, front-loaded loads, 16x16 and 32x32 bf16 blocks,
 fp32 blocks over two sub-slices; with and without the bias + GELU
-epilogue; and the patch kernel's configurations) are compiled for gfx950
+epilogue; and the patch kernels' configurations) are compiled for gfx950
 and must use no scratch memory.  A helper
 lambda that the compiler leaves as a call passes its captures through
 scratch, which made such kernels 10-100x slower; an array of uint4 kept
@@ -43,6 +43,15 @@ PATCH_INSTANCES = [
 ]
 
 
+# <TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR>
+PFIX_INSTANCES = [
+    "28, 32, 32, 16, 2, 3, 3, 2, 2, 4, 1, 1, 1",
+    "16, 32, 32, 16, 2, 3, 3, 2, 2, 4, 0, 1, 1",
+    "16, 28, 32, 16, 2, 3, 3, 2, 2, 2, 1, 1, 0",
+    "8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
+]
+
+
 def _resource_usage(header, kernel, params, instances):
     lines = ['#include "%s"' % header, "namespace convfwd {"]
     for inst in instances:
@@ -78,4 +87,10 @@ def test_dma_kernels_use_no_scratch():
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
 def test_patch_kernels_use_no_scratch():
     bad = _resource_usage("patch_kernel.h", "patch_conv_kernel", "PatchParams", PATCH_INSTANCES)
+    assert not bad, bad
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")
+def test_fixed_filter_patch_kernels_use_no_scratch():
+    bad = _resource_usage("patch_fixed.h", "patch_fixed_kernel", "PatchFixedParams", PFIX_INSTANCES)
     assert not bad, bad
