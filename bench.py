@@ -322,6 +322,7 @@ def layer_record(r, k, us, workload):
 def measure(r, steps, warmup, launches, workload):
     """Warm-up, the timed cold steps, the timed warm steps and the dedicated
     cold per-kernel pass of one workload."""
+    import numpy as np
     for _ in range(warmup):
         r.step(r.sets[0])
     nsets, sb = r.make_cold_sets()
