@@ -239,21 +239,30 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
                      [&](int j) { ldw(t0 + g + d + S::D1, d, j); });
         }
         if (half == 1) __syncthreads();   // every wave is done with the input patch
-        // h = bf16(act(acc + b1)), zeros outside the sequence (conv2's padding)
+        // h = bf16(act(acc + b1)), zeros outside the sequence (conv2's padding).
+        // Channel runs outermost, so each run's four biases are read once for
+        // all row blocks; the next run's are read before this run's h stores
+        // (which the compiler cannot tell apart from the bias words, so a read
+        // placed after them would wait for its whole latency).
+        f32x4_t bnext = BIAS ? *reinterpret_cast<const f32x4_t *>(bias_lds + wave * 96 + kh * 4)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mb = 0; mb < S::MBH; ++mb) {
-            const int r = half * 32 * S::MBH + mb * 32 + frow;
-            const bool inside = (unsigned)(hp0 + r) < (unsigned)cp.L;
+        for (int j = 0; j < 3; ++j)
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+            for (int hh = 0; hh < 4; ++hh) {
+                const int ch = wave * 96 + j * 32 + hh * 8 + kh * 4;
+                const f32x4_t bcur = bnext;
+                if (BIAS && j * 4 + hh < 11)
+                    bnext = *reinterpret_cast<const f32x4_t *>(bias_lds + ch + 8);
 #pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const int ch = wave * 96 + j * 32 + hh * 8 + kh * 4;
+                for (int mb = 0; mb < S::MBH; ++mb) {
+                    const int r = half * 32 * S::MBH + mb * 32 + frow;
+                    const bool inside = (unsigned)(hp0 + r) < (unsigned)cp.L;
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         float t = acc[mb][j][hh * 4 + e];
-                        if constexpr (BIAS) t += bias_lds[ch + e];
+                        if constexpr (BIAS) t += bcur[e];
                         if constexpr (GELU) t = gelu_erf_bf16out(t);
                         v[e] = inside ? t : 0.f;
                     }
@@ -262,7 +271,7 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
                     pk.y = f32x2_to_bf16x2(v[2], v[3]);
                     *reinterpret_cast<uint2 *>(hs + r * S::HP + (((ch >> 3) ^ ((r >> 1) & 15)) << 4) + (ch & 7) * 2) = pk;
                 }
-        }
+            }
     };
     conv1_half(0);
     conv1_half(1);
@@ -310,21 +319,26 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
     __syncthreads();              // every wave is done with h
 
     // ---- epilogue: bias, activation, bf16, staged in LDS, 16-byte stores ----
+    // (channel runs outermost, biases read one run ahead, as for h)
     unsigned char *Ys = hs;
+    f32x4_t bnext = BIAS ? *reinterpret_cast<const f32x4_t *>(bias_lds + K + wave * 96 + kh * 4)
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < S::MB2; ++mb) {
-        const int o = mb * 32 + frow;
-        if (o < S::TO) {
+    for (int j = 0; j < 3; ++j)
 #pragma unroll
-            for (int j = 0; j < 3; ++j)
+        for (int hh = 0; hh < 4; ++hh) {
+            const int ch = wave * 96 + j * 32 + hh * 8 + kh * 4;
+            const f32x4_t bcur = bnext;
+            if (BIAS && j * 4 + hh < 11) bnext = *reinterpret_cast<const f32x4_t *>(bias_lds + K + ch + 8);
 #pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const int ch = wave * 96 + j * 32 + hh * 8 + kh * 4;
+            for (int mb = 0; mb < S::MB2; ++mb) {
+                const int o = mb * 32 + frow;
+                if (o < S::TO) {
                     float v[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         float t = acc2[mb][j][hh * 4 + e];
-                        if constexpr (BIAS) t += bias_lds[K + ch + e];
+                        if constexpr (BIAS) t += bcur[e];
                         if constexpr (GELU) t = gelu_erf_bf16out(t);
                         v[e] = t;
                     }
@@ -333,8 +347,8 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
                     pk.y = f32x2_to_bf16x2(v[2], v[3]);
                     *reinterpret_cast<uint2 *>(Ys + o * S::YP + ch * 2) = pk;
                 }
+            }
         }
-    }
     __syncthreads();
     uint16_t *yg = reinterpret_cast<uint16_t *>(cp.y);
     constexpr int VPR = K / 8;    // 16-byte vectors per output row

@@ -662,23 +662,35 @@ igemm_dma_kernel(DmaParams dp)
     // 4*fk + e (e = 0..3) of pixel frow; in a 32x32 block it holds channels
     // 8*h + 4*fk + e (h = 0..3, e = 0..3) of pixel frow.
     T *Cs = reinterpret_cast<T *>(smem);
-    if (kg == 0) {
+    // Biases kept in LDS during the loop come to registers once, all reads
+    // issued together, before any output is staged (a read placed after the
+    // staging stores, which the compiler cannot tell apart from the bias
+    // words, would wait for its whole latency in every row block).
+    f32x4_t bias_l[S::BIAS_LDS && BIAS ? S::NI : 1][RUNS];
+    if constexpr (BIAS && S::BIAS_LDS) {
 #pragma unroll
-    for (int j = 0; j < S::NI; ++j)
+        for (int j = 0; j < S::NI; ++j)
 #pragma unroll
-        for (int h = 0; h < RUNS; ++h) {
-            const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BIAS && S::BIAS_LDS) {
-                const f32x4_t t4 = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF + nl * 4);
+            for (int h = 0; h < RUNS; ++h)
+                bias_l[j][h] = *reinterpret_cast<const f32x4_t *>(smem + S::BIAS_OFF +
+                                                                  (wn * S::TN + j * MF + h * 8 + fk * 4) * 4);
+    }
+    // Row block i of every wave: bias, activation and rounding of its
+    // accumulators, written to the tile's rows wm*TM + i*MF + frow in LDS.
+    auto stage_rows = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = t4[e];
-            } else if constexpr (BIAS) {
+        for (int j = 0; j < S::NI; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = bias_v[j][h][e];
-            }
+            for (int h = 0; h < RUNS; ++h) {
+                const int nl = wn * S::TN + j * MF + h * 8 + fk * 4;
+                float bv[4] = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BIAS && S::BIAS_LDS) {
 #pragma unroll
-            for (int i = 0; i < S::MI; ++i) {
+                    for (int e = 0; e < 4; ++e) bv[e] = bias_l[j][h][e];
+                } else if constexpr (BIAS) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = bias_v[j][h][e];
+                }
                 const int ml = wm * S::TM + i * MF + frow;
                 float v[4];
 #pragma unroll
@@ -695,11 +707,12 @@ igemm_dma_kernel(DmaParams dp)
                     *reinterpret_cast<f32x4_t *>(Cs + ml * S::LDC + nl) = f32x4_t{v[0], v[1], v[2], v[3]};
                 }
             }
-        }
-    }
-    __syncthreads();
+    };
 
     if (!p.out_vec) {   // K not a whole number of vectors: element stores
+#pragma unroll
+        for (int i = 0; i < S::MI; ++i) stage_rows(i);
+        __syncthreads();
         for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
             const int row = idx / OVPR;
             const int cv = idx % OVPR;
@@ -713,26 +726,41 @@ igemm_dma_kernel(DmaParams dp)
         }
         return;
     }
-    // Whole 16-byte vectors: every read from LDS is issued before any store,
-    // so the reads' latency is paid once (indices past the tile are clamped
-    // for the reads and skipped for the stores).
-    constexpr int NV = BM * OVPR;
-    constexpr int ITERS = (NV + S::NT - 1) / S::NT;
-    i32x4_t val[ITERS];   // (a native vector type: an array of uint4 is kept in scratch)
+    // Whole 16-byte vectors, one row block at a time: block i of every wave
+    // is staged, then its rows (MF rows of each of the WM wave rows) are read
+    // back and stored while the waves go on to stage block i + 1, so the
+    // stores of one block drain during the activation work of the next
+    // instead of all of them after all of it.  Blocks occupy disjoint LDS
+    // rows, so one barrier per block suffices.  Within a block every read is
+    // issued before any store (indices past the block are clamped for the
+    // reads and skipped for the stores).
+    constexpr int PROWS = WM * MF;                  // tile rows of one block
+    constexpr int NVP = PROWS * OVPR;
+    constexpr int ITERS = (NVP + S::NT - 1) / S::NT;
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int idx0 = tid + it * S::NT;
-        const int idx = idx0 < NV ? idx0 : NV - 1;
-        val[it] = *reinterpret_cast<const i32x4_t *>(Cs + (idx / OVPR) * S::LDC + (idx % OVPR) * S::VEC);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < S::MI; ++i) {
+        stage_rows(i);
+        __syncthreads();
+        i32x4_t val[ITERS];   // (a native vector type: an array of uint4 is kept in scratch)
+        int row_of[ITERS];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int idx = tid + it * S::NT;
-        const int m = m0 + idx / OVPR;
-        const int n = n0 + (idx % OVPR) * S::VEC;
-        if (idx < NV && m < p.M && n < p.K)
-            *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
+        for (int it = 0; it < ITERS; ++it) {
+            const int idx0 = tid + it * S::NT;
+            const int idx = idx0 < NVP ? idx0 : NVP - 1;
+            const int pr = idx / OVPR;
+            const int row = (pr / MF) * S::TM + i * MF + (pr % MF);
+            row_of[it] = row;
+            val[it] = *reinterpret_cast<const i32x4_t *>(Cs + row * S::LDC + (idx % OVPR) * S::VEC);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const int idx = tid + it * S::NT;
+            const int m = m0 + row_of[it];
+            const int n = n0 + (idx % OVPR) * S::VEC;
+            if (idx < NVP && m < p.M && n < p.K)
+                *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
+        }
     }
 }
 

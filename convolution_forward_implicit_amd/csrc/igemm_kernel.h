@@ -102,19 +102,20 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
 }
 
 // Exact GELU, t * Phi(t), branch-free and short (the epilogue of a
-// thin-reduction conv is bound by it).  With a = min(|t|, 6):
-// Phi(-a) = 2^R(a), R the degree-7 least-squares fit of log2 Phi(-a) on
-// [0, 6] at Chebyshev nodes, within 5.7e-6 (so Phi(-a) within 4e-6
-// relative); one exp2, seven FMAs, no reciprocal.  The result is t times
-// Phi(t) = 1 - Phi(-|t|) for t >= +0 and Phi(-|t|) for t <= -0, the choice
-// made from t's sign bit by a bit-field select (no compare, so no
-// condition-register hazard): neither form cancels.  Beyond |t| = 6 the
-// clamped Phi(-6) = 1e-9 leaves an absolute error below 1e-9 |t|.  NaN
-// propagates through the product, +inf maps to +inf and -inf to -inf
-// (t * Phi(-6)).
+// thin-reduction conv is bound by it).  With a = |t|: Phi(-a) = 2^R(a), R
+// the degree-7 least-squares fit of log2 Phi(-a) on [0, 6] at Chebyshev
+// nodes, within 5.7e-6 (so Phi(-a) within 4e-6 relative); one exp2, seven
+// FMAs, no reciprocal.  R is not clamped: past 6 it keeps decreasing, below
+// the fit's value at 6 (log2 Phi(-6) = -29.9) for every larger a and to
+// -inf for huge ones, so Phi(-a) only shrinks towards 0 there (checked
+// against its extrapolation on the CPU).  The result is t times Phi(t) =
+// 1 - Phi(-|t|) for t >= +0 and Phi(-|t|) for t <= -0, the choice made from
+// t's sign bit by a bit-field select (no compare, so no condition-register
+// hazard): neither form cancels.  NaN propagates, +inf maps to +inf and
+// -inf to NaN (-inf times Phi(-inf) = 0, as t/2 * erfc(-t/sqrt 2) gives).
 __device__ __forceinline__ float gelu_erf(float v)
 {
-    const float a = fminf(fabsf(v), 6.0f);
+    const float a = fabsf(v);
     float r = -1.889570263e-06f;
     r = fmaf(r, a, 6.268018558e-05f);
     r = fmaf(r, a, -9.388573895e-04f);
@@ -133,16 +134,17 @@ __device__ __forceinline__ float gelu_erf(float v)
 // Same t * Phi(t), cut to the output's precision: R is the degree-5
 // least-squares fit of log2 Phi(-a) on [0, 6] at Chebyshev nodes, within
 // 5.9e-4 (Phi(-a) within 4.1e-4 relative, a tenth of the output's rounding
-// step), and t * Phi(t) is formed as t/2 + |t| (1/2 - Phi(-|t|)), one fused
-// multiply-add with no sign test.  Four vector operations fewer per value
-// than gelu_erf.  For t < 0 the two terms nearly cancel, so the rounding of
-// 1/2 - Phi(-|t|) leaves an absolute error up to 2^-25 |t|: half an fp32
-// rounding of t itself, inside the error that the fp32 sum producing t
-// already carries.  NaN propagates, +inf maps to +inf, -inf to NaN (as
-// t/2 * erfc(-t/sqrt 2) does).
+// step), again unclamped (below -29.9 and decreasing past 6), and t * Phi(t)
+// is formed as t/2 + |t| (1/2 - Phi(-|t|)), one fused multiply-add with no
+// sign test.  Four vector operations fewer per value than gelu_erf.  For
+// t < 0 the two terms nearly cancel, so the rounding of 1/2 - Phi(-|t|)
+// leaves an absolute error up to 2^-25 |t|: half an fp32 rounding of t
+// itself, inside the error that the fp32 sum producing t already carries.
+// NaN propagates, +inf maps to +inf, -inf to NaN (as t/2 * erfc(-t/sqrt 2)
+// does).
 __device__ __forceinline__ float gelu_erf_bf16out(float v)
 {
-    const float a = fminf(fabsf(v), 6.0f);
+    const float a = fabsf(v);
     float r = -1.975036866e-04f;
     r = fmaf(r, a, 4.405779764e-03f);
     r = fmaf(r, a, -4.251449928e-02f);

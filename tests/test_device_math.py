@@ -22,31 +22,33 @@ def _device_gelu_coefficients(fn="gelu_erf", degree=7):
 def _device_gelu_f32(v):
     f = np.float32
     v = np.asarray(v, dtype=np.float32)
-    a = np.minimum(np.abs(v), f(6.0))
+    a = np.abs(v)
     c = _device_gelu_coefficients()
     r = np.full(v.shape, c[0], dtype=np.float32)
-    for k in c[1:]:   # fmaf: one rounding of the exact a*r + k
-        r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
-    p = np.exp2(r.astype(np.float64)).astype(np.float32)
-    q = np.where(np.signbit(v), p, (f(1.0) - p).astype(np.float32))
-    return (v * q).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for k in c[1:]:   # fmaf: one rounding of the exact a*r + k
+            r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
+        p = np.exp2(r.astype(np.float64)).astype(np.float32)
+        q = np.where(np.signbit(v), p, (f(1.0) - p).astype(np.float32))
+        return (v * q).astype(np.float32)
 
 
 def test_device_gelu_special_values():
-    v = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e30], dtype=np.float32)
+    v = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e30, -1e30], dtype=np.float32)
     g = _device_gelu_f32(v)
-    assert np.isnan(g[0]) and g[1] == np.inf and g[2] == -np.inf
+    # -inf: -inf * Phi(-inf) = -inf * 0, NaN as in t/2 * erfc(-t/sqrt 2)
+    assert np.isnan(g[0]) and g[1] == np.inf and np.isnan(g[2])
     assert g[3] == 0.0 and g[4] == 0.0
-    assert g[5] == np.float32(1e30)
+    assert g[5] == np.float32(1e30) and g[6] == 0.0
 
 
 def test_device_gelu_polynomial_accuracy():
-    t = np.concatenate([np.linspace(-12.0, 12.0, 480001), np.linspace(-1e-3, 1e-3, 2001)]).astype(np.float32)
+    t = np.concatenate([np.linspace(-40.0, 40.0, 800001), np.linspace(-1e-3, 1e-3, 2001)]).astype(np.float32)
     exact = np.array([0.5 * float(x) * math.erfc(-float(x) / math.sqrt(2.0)) for x in t.astype(np.float64)])
     got = _device_gelu_f32(t).astype(np.float64)
     err = np.abs(got - exact)
     # relative accuracy wherever the value is not tiny; where it is (the
-    # negative tail, Phi clamped at Phi(-6) = 1e-9 beyond |t| = 6) within
+    # negative tail beyond the fitted range, where R extrapolates) within
     # 1e-9 |t|, far inside the error bound the parity tests grade with
     big = np.abs(exact) > 1e-6
     assert np.max(err[big] / np.abs(exact[big])) < 1.2e-5
@@ -68,11 +70,12 @@ def test_device_gelu_polynomial_accuracy():
 def _device_gelu_bf16out_f32(v):
     f = np.float32
     v = np.asarray(v, dtype=np.float32)
-    a = np.minimum(np.abs(v), f(6.0))
+    a = np.abs(v)
     c = _device_gelu_coefficients("gelu_erf_bf16out", 5)
     r = np.full(v.shape, c[0], dtype=np.float32)
-    for k in c[1:]:
-        r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for k in c[1:]:
+            r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
     p = np.exp2(r.astype(np.float64)).astype(np.float32)
     h = (f(0.5) - p).astype(np.float32)
     half = (f(0.5) * v).astype(np.float32)
@@ -94,8 +97,7 @@ def test_device_gelu_bf16out_accuracy():
     got = _device_gelu_bf16out_f32(t).astype(np.float64)
     err = np.abs(got - exact)
     # a tenth of bfloat16's relative rounding step (2^-9), plus the
-    # absolute 2^-25 |t| of the cancelling negative side (and the clamp
-    # beyond |t| = 6, smaller still)
+    # absolute 2^-25 |t| of the cancelling negative side
     assert np.all(err <= 4.2e-4 * np.abs(exact) + 2.0 ** -24 * np.abs(t.astype(np.float64)))
     # the fit itself: log2 Phi(-a) within 6e-4 on [0, 6]
     a = np.linspace(0.0, 6.0, 60001)
@@ -106,3 +108,20 @@ def test_device_gelu_bf16out_accuracy():
     s = np.linspace(0.0, 5.0, 501).astype(np.float32)
     d = _device_gelu_bf16out_f32(s).astype(np.float64) - _device_gelu_bf16out_f32(-s)
     assert np.max(np.abs(d - s)) <= 2.0 ** -22 * 5.0
+
+
+def test_device_gelu_fits_extrapolate_downwards():
+    """Neither fit is clamped at |t| = 6: evaluated in float32 as the device
+    does, R stays below its value at 6 (log2 Phi(-6) = -29.9) and keeps
+    decreasing for every larger a, up to overflow to -inf, so Phi(-a) =
+    2^R only shrinks towards 0 there."""
+    a = np.concatenate([np.linspace(6.0, 100.0, 200001), np.geomspace(100.0, 3e38, 20001)]).astype(np.float32)
+    for fn, deg in (("gelu_erf", 7), ("gelu_erf_bf16out", 5)):
+        c = _device_gelu_coefficients(fn, deg)
+        r = np.full(a.shape, c[0], dtype=np.float32)
+        with np.errstate(over="ignore", invalid="ignore"):
+            for k in c[1:]:
+                r = (a.astype(np.float64) * r.astype(np.float64) + np.float64(np.float32(k))).astype(np.float32)
+        assert not np.isnan(r).any()
+        assert np.all(r <= -29.9) and np.all(r[1:] <= r[:-1]), fn
+        assert r[-1] == -np.inf
