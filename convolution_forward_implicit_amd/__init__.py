@@ -66,6 +66,12 @@ class ConvFwd:
     def describe(self):
         return capi.conv_fwd_describe(self._plan)
 
+    def packed_config(self):
+        """Index of the tile configuration pack / run_packed use (the
+        plan's own, or the one a tuning record names for prepacked
+        weights)."""
+        return capi.conv_fwd_packed_config(self._plan)
+
     def packed_bytes(self):
         """Size of this plan's prepacked weights (ConvError UNSUPPORTED when
         the plan's kernel reads natural weights only)."""

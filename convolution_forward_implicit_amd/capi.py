@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "CONV_OK", 1: "CONV_ERR_INVALID_ARG", 2: "CONV_ERR_UNSUPPORTE
                 3: "CONV_ERR_HIP", 4: "CONV_ERR_NOMEM"}
 
 EXPORTED = ["conv_fwd_create", "conv_fwd_create_with_config", "conv_fwd_out_dims", "conv_fwd_useful_flop",
-            "conv_fwd_packed_bytes", "conv_fwd_pack_weights", "conv_fwd_run_packed", "conv_fwd_run_packed_events",
+            "conv_fwd_packed_config", "conv_fwd_packed_bytes", "conv_fwd_pack_weights", "conv_fwd_run_packed", "conv_fwd_run_packed_events",
             "conv_fwd_run", "conv_fwd_run_events", "conv_fwd_destroy", "conv_fwd_describe", "conv_fwd_num_configs",
             "conv_fwd_config_name", "conv_fwd_config_dtype", "conv_fwd_last_error",
             "conv_chain_create", "conv_chain_run", "conv_chain_run_events", "conv_chain_destroy",
@@ -74,6 +74,8 @@ def lib():
         L.conv_fwd_out_dims.restype = ctypes.c_int
         L.conv_fwd_useful_flop.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
         L.conv_fwd_useful_flop.restype = ctypes.c_int
+        L.conv_fwd_packed_config.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+        L.conv_fwd_packed_config.restype = ctypes.c_int
         L.conv_fwd_packed_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
         L.conv_fwd_packed_bytes.restype = ctypes.c_int
         L.conv_fwd_pack_weights.argtypes = [P, P, P, P]
@@ -186,6 +188,12 @@ def conv_fwd_out_dims(plan):
 def conv_fwd_useful_flop(plan):
     n = ctypes.c_int64()
     _check(lib().conv_fwd_useful_flop(plan, ctypes.byref(n)))
+    return n.value
+
+
+def conv_fwd_packed_config(plan):
+    n = ctypes.c_int32()
+    _check(lib().conv_fwd_packed_config(plan, ctypes.byref(n)))
     return n.value
 
 

@@ -255,6 +255,8 @@ const TileCfg kCfgs[] = {
     PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PFIX(16, 32, 32, 16, 2, 3, 3, 1, 1, 4, 0, 1, 1),
     PFIX(8, 32, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
+    PFIX(4, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
+    PFIX(4, 56, 64, 16, 2, 3, 3, 1, 1, 2, 1, 1, 0),
     PATCH(8, 32, 64, 16, 2, 10, 34, 9, 1),
     PATCH(4, 32, 64, 16, 2, 6, 34, 9, 1),
     PATCH(8, 32, 32, 16, 2, 12, 36, 9, 1),
@@ -340,22 +342,35 @@ const CostCoef kCoef[] = {
 
 // Exact-shape tuning records: for every problem of the calibration sweep,
 // the configuration measured fastest on MI355X (256 compute units), with and
-// without the GELU epilogue (tuning/fit.py writes them from the sweep).  A
-// plan for one of these shapes (the bias flag is ignored) on a device with
-// that many compute units takes the record; every other shape is decided by
-// the fitted cost model.
+// without the GELU epilogue, and the one measured fastest from prepacked
+// weights (tuning/fit.py writes them from the sweep; "" when no
+// configuration with a prepacked form fits the problem).  A plan for one of
+// these shapes (the bias flag is ignored) on a device with that many compute
+// units takes the record; every other shape is decided by the fitted cost
+// model, and its prepacked entry points use the same configuration.
 struct TuneRec {
     int32_t dtype, gelu;
     int64_t N, G, C, K, in[3], filt[3], stride[3], pad[3], dil[3];
     const char *config;
+    const char *packed_config;
 };
 const TuneRec kTuneDb[] = {
 #include "selector_db.inc"
 };
 constexpr int kTuneCus = 256;
 
-int tuned_config(const conv_fwd_desc_t &d)
+int config_index(const char *name)
 {
+    for (int i = 0; i < kNumCfgs; ++i)
+        if (strcmp(kCfgs[i].name, name) == 0) return i;
+    return -1;
+}
+
+// The record for the problem: its configuration (or -1) and, in *packed,
+// its prepacked-weight configuration (or -1).
+int tuned_config(const conv_fwd_desc_t &d, int *packed)
+{
+    *packed = -1;
     for (const TuneRec &t : kTuneDb) {
         bool same = t.dtype == d.dtype && t.gelu == d.gelu && t.N == d.N && t.G == d.G && t.C == d.C &&
                     t.K == d.K;
@@ -363,8 +378,8 @@ int tuned_config(const conv_fwd_desc_t &d)
             same = t.in[i] == d.in[i] && t.filt[i] == d.filt[i] && t.stride[i] == d.stride[i] &&
                    t.pad[i] == d.pad[i] && t.dil[i] == d.dilation[i];
         if (!same) continue;
-        for (int i = 0; i < kNumCfgs; ++i)
-            if (strcmp(kCfgs[i].name, t.config) == 0) return i;
+        *packed = config_index(t.packed_config);
+        return config_index(t.config);
     }
     return -1;
 }
@@ -450,7 +465,10 @@ struct conv_fwd_plan {
     KParams kp;      // pointers filled per run
     PackParams pk;   // prepacked weights: pointers filled per call
     int64_t packed_bytes;   // 0: the plan's kernel reads natural weights only
-    char text[256];
+    // The prepacked entry points' plan when a tuning record names another
+    // configuration for them (owned), else null: they use this plan.
+    conv_fwd_plan *packed_plan;
+    char text[320];
 };
 
 namespace {
@@ -684,10 +702,21 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
         pl->cfg = forced;
     } else {
         const int cus = device_cu_count();
-        const int rec = cus == kTuneCus ? tuned_config(d) : -1;
+        int prec = -1;
+        const int rec = cus == kTuneCus ? tuned_config(d, &prec) : -1;
         if (rec >= 0 && eligible(kCfgs[rec])) {
             pl->cfg = rec;
             pl->tuned = true;
+            if (prec >= 0 && prec != rec && eligible(kCfgs[prec])) {
+                conv_fwd_plan *pp = nullptr;
+                st = create_impl(desc, prec, &pp);
+                if (st != CONV_OK) {
+                    delete pl;
+                    return st;
+                }
+                pp->tuned = true;
+                pl->packed_plan = pp;
+            }
         } else {
             int best = -1;
             double best_cost = 0.0;
@@ -749,6 +778,7 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     pk.slots = pl->packed_bytes / 16;
     const double grid = tiles_of(c, d, out);
     if (grid >= 2147483647.0) {
+        delete pl->packed_plan;
         delete pl;
         return fail(CONV_ERR_UNSUPPORTED, "grid too large");
     }
@@ -763,6 +793,11 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
                  "igemm %s M=%d N=%d Kred=%d G=%d grid=%d (%dx%dx%d tiles) lds=%dB%s",
                  c.name, kp.M, kp.K, kp.Kred, kp.G, pl->grid, kp.tiles_m, kp.tiles_n, kp.G, c.lds_bytes,
                  forced >= 0 ? " forced" : pl->tuned ? " tuned" : "");
+    if (pl->packed_plan) {
+        const size_t n = strlen(pl->text);
+        snprintf(pl->text + n, sizeof(pl->text) - n, "; prepacked: %s grid=%d", kCfgs[pl->packed_plan->cfg].name,
+                 pl->packed_plan->grid);
+    }
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
     return CONV_OK;
@@ -815,8 +850,22 @@ conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, co
     return run_impl(plan, x, w, bias, y, stream, start_event, stop_event, false);
 }
 
+// The plan the prepacked entry points run.
+static const conv_fwd_plan_t *packed_of(const conv_fwd_plan_t *plan)
+{
+    return plan && plan->packed_plan ? plan->packed_plan : plan;
+}
+
+conv_status_t conv_fwd_packed_config(const conv_fwd_plan_t *plan, int32_t *config)
+{
+    if (!plan || !config) return fail(CONV_ERR_INVALID_ARG, "plan or config is NULL");
+    *config = packed_of(plan)->cfg;
+    return CONV_OK;
+}
+
 conv_status_t conv_fwd_packed_bytes(const conv_fwd_plan_t *plan, int64_t *bytes)
 {
+    plan = packed_of(plan);
     if (!plan || !bytes) return fail(CONV_ERR_INVALID_ARG, "plan or bytes is NULL");
     if (plan->packed_bytes == 0)
         return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
@@ -827,6 +876,7 @@ conv_status_t conv_fwd_packed_bytes(const conv_fwd_plan_t *plan, int64_t *bytes)
 
 conv_status_t conv_fwd_pack_weights(const conv_fwd_plan_t *plan, const void *w, void *packed, void *stream)
 {
+    plan = packed_of(plan);
     if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
     if (plan->packed_bytes == 0)
         return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
@@ -851,6 +901,7 @@ conv_status_t conv_fwd_run_packed_events(const conv_fwd_plan_t *plan, const void
                                          const void *bias, void *y, void *stream, void *start_event,
                                          void *stop_event)
 {
+    plan = packed_of(plan);
     if (plan && plan->packed_bytes == 0)
         return fail(CONV_ERR_UNSUPPORTED, "the plan's kernel (%s) reads natural weights only",
                     kCfgs[plan->cfg].name);
@@ -900,7 +951,11 @@ conv_status_t conv_fwd_run(const conv_fwd_plan_t *plan, const void *x, const voi
     return conv_fwd_run_events(plan, x, w, bias, y, stream, nullptr, nullptr);
 }
 
-void conv_fwd_destroy(conv_fwd_plan_t *plan) { delete plan; }
+void conv_fwd_destroy(conv_fwd_plan_t *plan)
+{
+    if (plan) delete plan->packed_plan;
+    delete plan;
+}
 
 const char *conv_fwd_describe(const conv_fwd_plan_t *plan) { return plan ? plan->text : ""; }
 

@@ -77,8 +77,10 @@ def load(path):
                 v = [int(x) for x in key[1:]]
                 probs[key] = {"dtype": key[0], "N": v[0], "G": v[1], "C": v[2], "K": v[3],
                               "in": v[4:7], "filt": v[7:10], "stride": v[10:13], "pad": v[13:16],
-                              "dil": v[16:19], "gelu": v[19], "times": {}}
+                              "dil": v[16:19], "gelu": v[19], "times": {}, "ptimes": {}}
             probs[key]["times"][row["config"]] = float(row["ms"])
+            if row.get("ms_packed"):
+                probs[key]["ptimes"][row["config"]] = float(row["ms_packed"])
     return list(probs.values())
 
 
@@ -146,37 +148,40 @@ def packable(name):
     return "_dma_" in name or "_pfix_" in name
 
 
-def record(times):
-    """The tuning record of one swept (problem, epilogue): the fastest
-    configuration, or the fastest one with a prepacked-weight form when it
-    is within PACK_TOLERANCE of it (a plan serves both the natural and the
-    prepacked entry points, and prepacked weights only help kernels that
-    have that form)."""
+def record(p):
+    """The tuning record of one swept (problem, epilogue): (configuration,
+    prepacked-weight configuration).  With prepacked timings in the sweep:
+    the fastest configuration from natural weights and, separately, the
+    fastest from prepacked weights (a plan holds both).  Without them: the
+    fastest configuration, or the fastest one with a prepacked form when it
+    is within PACK_TOLERANCE of it, serving both entry points."""
+    times, ptimes = p["times"], p.get("ptimes", {})
     best = min(times, key=times.get)
-    if packable(best):
-        return best
-    pk = [n for n in times if packable(n)]
-    if pk:
-        alt = min(pk, key=times.get)
-        if times[alt] <= PACK_TOLERANCE * times[best]:
-            return alt
-    return best
+    if ptimes:
+        return best, min(ptimes, key=ptimes.get)
+    if not packable(best):
+        pk = [n for n in times if packable(n)]
+        if pk:
+            alt = min(pk, key=times.get)
+            if times[alt] <= PACK_TOLERANCE * times[best]:
+                best = alt
+    return best, best if packable(best) else ""
 
 
 def write_db(probs, path=OUT_DB):
     """Exact-shape tuning records: per swept (problem, epilogue), the
-    fastest measured configuration (see record)."""
+    fastest measured configurations (see record)."""
     with open(path, "w") as f:
-        f.write("// Generated by convolution_forward_implicit_amd/tuning/fit.py: the configuration\n"
+        f.write("// Generated by convolution_forward_implicit_amd/tuning/fit.py: the configurations\n"
                 "// measured fastest for each problem of the calibration sweep (MI355X, 256 CUs),\n"
-                "// or one with a prepacked-weight form within 3% of it.\n"
-                "// {dtype, gelu, N, G, C, K, in, filt, stride, pad, dil, config}\n")
+                "// from natural and from prepacked weights (\"\": none has a prepacked form).\n"
+                "// {dtype, gelu, N, G, C, K, in, filt, stride, pad, dil, config, packed config}\n")
         for p in probs:
-            best = record(p["times"])
+            best, pbest = record(p)
             t = lambda v: "{%d, %d, %d}" % tuple(v)
-            f.write('    {%d, %d, %d, %d, %d, %d, %s, %s, %s, %s, %s, "%s"},\n' % (
+            f.write('    {%d, %d, %d, %d, %d, %d, %s, %s, %s, %s, %s, "%s", "%s"},\n' % (
                 0 if p["dtype"] == "f32" else 1, p["gelu"], p["N"], p["G"], p["C"], p["K"], t(p["in"]),
-                t(p["filt"]), t(p["stride"]), t(p["pad"]), t(p["dil"]), best))
+                t(p["filt"]), t(p["stride"]), t(p["pad"]), t(p["dil"]), best, pbest))
 
 
 if __name__ == "__main__":

@@ -9,8 +9,10 @@ matters for thin reductions); the "gelu" column says which.  Timing: warm
 caches, 40 launches to raise the clock, then per configuration 3 untimed
 launches and the median of 21, each timed by HIP events that the launch
 records when the kernel starts and ends; all configurations are timed twice,
-in opposite orders, and the lower median is kept.  Inputs are
-random (values do not affect the timing).
+in opposite orders, and the lower median is kept.  A configuration with a
+prepacked-weight form is timed the same way from its prepacked weights too
+("ms_packed"; empty for the others).  Inputs are random (values do not
+affect the timing).
 """
 import csv
 import itertools
@@ -22,7 +24,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 FIELDS = ["dtype", "N", "G", "C", "K", "Di", "Hi", "Wi", "Z", "Y", "X", "sd", "sh", "sw",
-          "pd", "ph", "pw", "dd", "dh", "dw", "gelu", "config", "ms"]
+          "pd", "ph", "pw", "dd", "dh", "dw", "gelu", "config", "ms", "ms_packed"]
 
 
 def problem(N, G, C, K, inp, filt, stride, pad, dil):
@@ -77,18 +79,25 @@ def main(path):
             plans = []
             for ci, name in enumerate(names):
                 try:
-                    plans.append((name, ConvFwd(p, dt, ge, ge, config=ci)))
+                    c = ConvFwd(p, dt, ge, ge, config=ci)
                 except ConvError:
                     continue
+                plans.append((name, c, lambda c=c: c(x, w, b, out=y), lambda e, c=c: c(x, w, b, out=y, events=e)))
+                try:
+                    wp = c.pack(w)
+                except ConvError:
+                    continue
+                plans.append((name + " packed", c, lambda c=c, wp=wp: c.run_packed(x, wp, b, out=y),
+                              lambda e, c=c, wp=wp: c.run_packed(x, wp, b, out=y, events=e)))
             for _ in range(40):           # bring the clock up before anything is timed
                 ref(x, w, b, out=y)
             best = {}
             # two passes in opposite orders, the lower median kept: a clock that
             # is still rising favours no particular position in the table
             for order in (plans, plans[::-1]):
-                for name, c in order:
+                for name, c, run, run_ev in order:
                     for _ in range(3):
-                        c(x, w, b, out=y)
+                        run()
                     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                            for _ in range(21)]
                     for a, e in evs:      # create the event handles the launches record
@@ -96,14 +105,18 @@ def main(path):
                         e.record()
                     torch.cuda.synchronize()
                     for a, e in evs:      # kernel start/stop, without the launch gap
-                        c(x, w, b, out=y, events=(a, e))
+                        run_ev((a, e))
                     torch.cuda.synchronize()
                     ts = sorted(a.elapsed_time(e) for a, e in evs)
                     med = ts[len(ts) // 2]
                     best[name] = min(best.get(name, med), med)
-            for name, _ in plans:
+            for name, _, _, _ in plans:
+                if name.endswith(" packed"):
+                    continue
+                pk = best.get(name + " packed")
                 wr.writerow([dt, p["N"], p["G"], p["C"], p["K"], *p["in"], *p["filt"], *p["stride"],
-                             *p["pad"], *p["dil"], int(ge), name, "%.6f" % best[name]])
+                             *p["pad"], *p["dil"], int(ge), name, "%.6f" % best[name],
+                             "" if pk is None else "%.6f" % pk])
             f.flush()
             print("swept", dt, "gelu" if ge else "", p, flush=True)
 

@@ -138,9 +138,20 @@ conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, co
  * (group, output-channel tile, K-step), zeros wherever the kernel would
  * load nothing.  Each K-step then fetches its weights as contiguous
  * kilobytes.  It depends on the plan (its tile configuration), not only on
- * the problem: pack with the plan that runs.  Same results as conv_fwd_run
- * for the same weights, bit for bit (same kernel, same summation order).
+ * the problem: pack with the plan that runs.
  *
+ * The prepacked entry points of a plan may run another tile configuration
+ * than conv_fwd_run: where a tuning record names a faster one for prepacked
+ * weights (cheaper weight loads can favour, say, smaller boxes with two
+ * workgroups per compute unit), the plan holds both, and
+ * conv_fwd_packed_config says which the prepacked calls use.  Their
+ * results are those of conv_fwd_run with that configuration
+ * (conv_fwd_create_with_config), bit for bit (same kernel, same summation
+ * order), and meet the same error bound against the exact convolution.
+ *
+ * conv_fwd_packed_config: index of the configuration the prepacked entry
+ *   points run (the plan's own unless a tuning record names another);
+ *   INVALID_ARG for NULL arguments.
  * conv_fwd_packed_bytes: size of the packed weights (a multiple of 16).
  *   CONV_ERR_UNSUPPORTED if the plan's kernel reads natural weights only
  *   (the register-staged and the runtime-filter patch kernels), or the image
@@ -151,6 +162,7 @@ conv_status_t conv_fwd_run_events(const conv_fwd_plan_t *plan, const void *x, co
  *   overlapping.  Allocates nothing.
  * conv_fwd_run_packed(_events): as conv_fwd_run(_events) with the packed
  *   weights in place of w (16-byte aligned; y must not overlap it). */
+conv_status_t conv_fwd_packed_config(const conv_fwd_plan_t *plan, int32_t *config);
 conv_status_t conv_fwd_packed_bytes(const conv_fwd_plan_t *plan, int64_t *bytes);
 conv_status_t conv_fwd_pack_weights(const conv_fwd_plan_t *plan, const void *w, void *packed, void *stream);
 conv_status_t conv_fwd_run_packed(const conv_fwd_plan_t *plan, const void *x, const void *packed,

@@ -292,9 +292,54 @@ def test_tuning_records_match_sweep_and_configs(tmp_path):
     rows = [l for l in committed.splitlines() if l.strip().startswith("{")]
     assert len(rows) == len(probs)
     for l in rows:
-        name = l.split('"')[1]
+        name, packed = l.split('"')[1], l.split('"')[3]
         assert name in dtype_of, name
         assert dtype_of[name] == int(l.strip()[1]), l
+        # the prepacked-weight configuration: none, or a compiled one of the
+        # same dtype that has a prepacked form
+        assert packed == "" or (dtype_of.get(packed) == int(l.strip()[1]) and fit.packable(packed)), l
+
+
+def test_plans_take_the_records_prepacked_configuration():
+    """A plan for a recorded shape runs the record's configuration from
+    natural weights and the record's prepacked-weight configuration from
+    prepacked weights (conv_fwd_packed_config); a forced plan uses its own
+    configuration for both."""
+    import os
+    import re as _re
+    from convolution_forward_implicit_amd.tuning import fit
+    here = os.path.dirname(capi.LIB_PATH)
+    index = {capi.conv_fwd_config_name(i): i for i in range(capi.conv_fwd_num_configs())}
+    probs = fit.load(os.path.join(here, "tuning", "sweep_mi355x.csv"))
+    seen_split = 0
+    for p in probs:
+        best, pbest = fit.record(p)
+        prob = sd.problem(p["N"], p["G"], p["C"], p["K"], tuple(p["in"]), tuple(p["filt"]), tuple(p["stride"]),
+                          tuple(p["pad"]), tuple(p["dil"]))
+        plan = capi.conv_fwd_create(desc_from_problem(prob, p["dtype"], bool(p["gelu"]), bool(p["gelu"])))
+        try:
+            text = capi.conv_fwd_describe(plan)
+            assert (" %s " % best) in text and "tuned" in text, text
+            if pbest:
+                assert capi.conv_fwd_packed_config(plan) == index[pbest]
+                if pbest != best:
+                    seen_split += 1
+                    assert ("prepacked: %s " % pbest) in text, text
+            else:
+                assert capi.conv_fwd_packed_config(plan) == index[best]
+        finally:
+            capi.conv_fwd_destroy(plan)
+    if any(p["ptimes"] for p in probs):
+        assert seen_split > 0   # prepacked timings change some records
+    i = _cfg_index(r"^bf16_dma_128x64_w2x2_s2_m32_k1$")
+    plan = capi.conv_fwd_create_with_config(desc_from_problem(sd.conv1d_problem(2, 64, 64, 100, 3, 1, 1), "bf16"), i)
+    try:
+        assert capi.conv_fwd_packed_config(plan) == i
+        assert "prepacked:" not in capi.conv_fwd_describe(plan)
+    finally:
+        capi.conv_fwd_destroy(plan)
+    with pytest.raises(ConvError):
+        capi.conv_fwd_packed_config(None)
 
 
 # --------------------------------------------------------------------------

@@ -49,6 +49,7 @@ PFIX_INSTANCES = [
     "16, 32, 32, 16, 2, 3, 3, 2, 2, 4, 0, 1, 1",
     "16, 28, 32, 16, 2, 3, 3, 2, 2, 2, 1, 1, 0",
     "8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
+    "4, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
 ]
 
 

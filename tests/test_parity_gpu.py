@@ -252,8 +252,9 @@ def test_every_packable_config_prepacked_weights(dev, cfg, name):
 
 
 def _packed_plan_for(wid, li):
-    """The tile configuration the prepacked path runs a workload layer with:
-    the selector's, when it has a packed form."""
+    """The selector's plan for a workload layer when its prepacked entry
+    points have a kernel to run (its own configuration or the one a tuning
+    record names for prepacked weights)."""
     from convolution_forward_implicit_amd import ConvFwd, ConvError
     p, hb, ge = sd.layers(wid)[li]
     c = ConvFwd(p, sd.dtype_of(wid), hb, ge)
@@ -267,15 +268,17 @@ def _packed_plan_for(wid, li):
 @pytest.mark.parametrize("wid", [1, 2, 4, 5])
 def test_workload_prepacked_weights(dev, wid):
     """The workloads at full size with prepacked weights in the plan the
-    benchmark times: every output bit for bit the natural run, and against
-    the oracle at the per-element bound."""
+    benchmark times: every output bit for bit the natural run of the same
+    configuration (the one conv_fwd_packed_config names), and against the
+    oracle at the per-element bound."""
     W = sd.workload(wid)
     dt = W["dtype"]
     x = W["x"]
     for li, (p, hb, ge) in enumerate(W["layers"]):
-        if _packed_plan_for(wid, li) is None:
+        pl = _packed_plan_for(wid, li)
+        if pl is None:
             pytest.skip("the selector's kernel for this layer reads natural weights only")
-        yn, _ = run(dev, p, dt, x, W["w"][li], W["b"][li], ge)
+        yn, _ = run(dev, p, dt, x, W["w"][li], W["b"][li], ge, config=pl.packed_config())
         yp, c = run_packed(dev, p, dt, x, W["w"][li], W["b"][li], ge)
         assert same_bits(yn, yp)
         assert_close(host(yp), p, dt, x, W["w"][li], W["b"][li], ge)
