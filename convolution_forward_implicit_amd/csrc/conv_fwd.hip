@@ -252,11 +252,19 @@ const TileCfg kCfgs[] = {
     PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 4, 1, 1, 1),
     PFIX(16, 32, 32, 16, 2, 3, 3, 2, 2, 4, 0, 1, 1),
     PFIX(16, 28, 32, 16, 2, 3, 3, 2, 2, 2, 1, 1, 0),
+    PFIX(14, 32, 32, 16, 2, 3, 3, 2, 2, 2, 0, 1, 1),
+    PFIX(14, 32, 32, 16, 2, 3, 3, 2, 2, 7, 0, 1, 1),
+    PFIX(14, 32, 32, 16, 2, 3, 3, 2, 2, 14, 0, 1, 1),
+    PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 7, 1, 1, 1),
+    PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 14, 1, 1, 1),
     PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PFIX(16, 32, 32, 16, 2, 3, 3, 1, 1, 4, 0, 1, 1),
     PFIX(8, 32, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PFIX(4, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PFIX(4, 56, 64, 16, 2, 3, 3, 1, 1, 2, 1, 1, 0),
+    PFIX(4, 56, 64, 16, 2, 3, 3, 1, 1, 7, 0, 1, 0),
+    PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 7, 1, 1, 0),
+    PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 14, 1, 1, 0),
     PATCH(8, 32, 64, 16, 2, 10, 34, 9, 1),
     PATCH(4, 32, 64, 16, 2, 6, 34, 9, 1),
     PATCH(8, 32, 32, 16, 2, 12, 36, 9, 1),

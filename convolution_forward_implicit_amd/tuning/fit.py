@@ -36,7 +36,7 @@ def cfg_tile(name):
     m = re.match(r"bf16_patch_(\d+)x(\d+)x(\d+)_c(\d+)_s\d_p\d+x\d+_d\d$", name)
     if m:
         return ("patch",) + tuple(int(v) for v in m.groups())
-    m = re.match(r"bf16_pfix_(\d+)x(\d+)x(\d+)_c(\d+)_s\d_f\d+x\d+_d\d+x\d+_w\d_l\d_r\d_rr\d$", name)
+    m = re.match(r"bf16_pfix_(\d+)x(\d+)x(\d+)_c(\d+)_s\d_f\d+x\d+_d\d+x\d+_w\d+_l\d_r\d_rr\d$", name)
     if m:
         return ("patch",) + tuple(int(v) for v in m.groups())
     m = re.match(r"(f32|bf16)_dma_(\d+)x(\d+)_w\dx\d_s\d_m\d+_k(\d)(_g\d)?(_f\d)?$", name)

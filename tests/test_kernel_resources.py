@@ -50,6 +50,8 @@ PFIX_INSTANCES = [
     "16, 28, 32, 16, 2, 3, 3, 2, 2, 2, 1, 1, 0",
     "8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
     "4, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
+    "8, 56, 64, 16, 2, 3, 3, 1, 1, 7, 1, 1, 0",
+    "28, 32, 32, 16, 2, 3, 3, 2, 2, 14, 1, 1, 1",
 ]
 
 
