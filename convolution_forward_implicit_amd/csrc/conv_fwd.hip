@@ -223,6 +223,13 @@ struct TileCfg {
                 : "f32_dma_" #BM "x" #BN "_w1x1_s" #NS "_m" #MF "_k" #KSUB "_g4_f" #FL), \
             0, 0, 0, 0, 0, 0, 4, 0, 0, 0, 0, 0, MF}
 
+// Any wave grid, reduction groups and load spread, with its name spelled out
+#define DMAX(DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL, NAME)                               \
+    TileCfg{DT, KIND_DMA, BM, BN, KSUB * 128 / (DT ? 2 : 4), WM, WN, 16 / (DT ? 2 : 4), NS, \
+            DmaShape<DT, BM, BN, WM, WN, NS, MF, KSUB, KG>::LDS_BYTES,                    \
+            &launch_dma<DT, BM, BN, WM, WN, NS, MF, KSUB, KG, FL>, NAME,                  \
+            0, 0, 0, 0, 0, 0, KG, 0, 0, 0, 0, 0, MF}
+
 // Input-patch kernel (bf16): box TH x TW output pixels, BN output channels,
 // CC input channels per K-step, patch at most PHMAX x PWMAX, at most TAPMAX
 // filter taps per depth tap.
@@ -313,6 +320,10 @@ const TileCfg kCfgs[] = {
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
     DMA4(0, 48, 48, 2, 16, 1),
     DMA4F(0, 48, 48, 2, 16, 1, 4),
+    DMAX(0, 48, 48, 3, 1, 2, 16, 1, 4, 4, "f32_dma_48x48_w3x1_s2_m16_k1_g4_f4"),
+    DMAX(0, 48, 48, 1, 3, 2, 16, 1, 4, 4, "f32_dma_48x48_w1x3_s2_m16_k1_g4_f4"),
+    DMAX(0, 48, 96, 3, 2, 2, 16, 2, 2, 0, "f32_dma_48x96_w3x2_s2_m16_k2_g2"),
+    DMAX(0, 48, 96, 3, 2, 2, 16, 2, 2, 4, "f32_dma_48x96_w3x2_s2_m16_k2_g2_f4"),
     DMA4(0, 48, 48, 3, 16, 1),
     DMA2(0, 48, 96, 1, 2, 3, 16, 1),
     DMA2(0, 48, 96, 1, 2, 2, 16, 2),
