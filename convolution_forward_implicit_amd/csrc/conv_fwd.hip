@@ -264,6 +264,7 @@ const TileCfg kCfgs[] = {
     PFIX(14, 32, 32, 16, 2, 3, 3, 2, 2, 14, 0, 1, 1),
     PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 7, 1, 1, 1),
     PFIX(28, 32, 32, 16, 2, 3, 3, 2, 2, 14, 1, 1, 1),
+    PFIX(28, 28, 32, 16, 2, 3, 3, 2, 2, 13, 1, 1, 0),
     PFIX(8, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),
     PFIX(16, 32, 32, 16, 2, 3, 3, 1, 1, 4, 0, 1, 1),
     PFIX(8, 32, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0),

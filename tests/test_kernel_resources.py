@@ -52,6 +52,7 @@ PFIX_INSTANCES = [
     "4, 56, 64, 16, 2, 3, 3, 1, 1, 4, 1, 1, 0",
     "8, 56, 64, 16, 2, 3, 3, 1, 1, 7, 1, 1, 0",
     "28, 32, 32, 16, 2, 3, 3, 2, 2, 14, 1, 1, 1",
+    "28, 28, 32, 16, 2, 3, 3, 2, 2, 13, 1, 1, 0",
 ]
 
 
