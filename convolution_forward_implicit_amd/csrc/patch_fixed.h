@@ -66,7 +66,16 @@ struct PatchFixedShape {
     // (an odd number of 16-byte slots per pixel, so 16 consecutive pixels of
     // one chunk fall in 16 different bank groups)
     static constexpr int PPITCH = CPL + 1;             // slots per pixel (PM = 1)
-    static constexpr int PSLOTS = PM ? PPITCH * NPIX : CPL * NPIX;   // 16-byte patch slots
+    // Pixel-major rows of a flattened box (RR = 0) end with RSK pad slots:
+    // a 32-pixel fragment read that crosses a box row end jumps over the
+    // row's PW - TW halo pixels, and with RSK = -(PW - TW) * PPITCH mod 16
+    // that jump moves the slot index by PPITCH modulo 16 like any other
+    // pixel step, so the 16 lanes of a quarter-wave still hit 16 different
+    // 16-byte bank groups (without it the reads that straddle a row end
+    // were two-way conflicted: 0.33-0.6 conflict cycles per access).
+    static constexpr int RSK = (PM && !RR) ? (16 - ((PW - TW) * PPITCH) % 16) % 16 : 0;
+    static constexpr int ROWSLOTS = PW * PPITCH + RSK; // slots per patch row (PM = 1)
+    static constexpr int PSLOTS = PM ? ROWSLOTS * PH : CPL * NPIX;   // 16-byte patch slots
     static constexpr int PINST = (PSLOTS + 63) / 64;   // 1 KB loads of the patch (workgroup)
     static constexpr int WSLOTS = CPL * TAPS * BN;
     static constexpr int WINST = (WSLOTS + 63) / 64;
@@ -84,6 +93,7 @@ struct PatchFixedShape {
     static_assert(BN % 32 == 0 && CC % 16 == 0, "32x32x16 blocks");
     static_assert(PM == 0 || (PPITCH & 1), "odd pixel pitch");
     static_assert(!RR || (TW == 32 && NBLK == NW * MI), "row reuse: one 32-pixel box row per block, whole rows per wave");
+    static_assert(RSK == 0 || !RR, "row reuse addresses rows as PW * PPITCH slots");
     static_assert(NS >= 2 && L * (NS - 2) < 64, "vmcnt budget");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS of one CU");
 };
@@ -143,22 +153,27 @@ patch_fixed_kernel(PatchFixedParams pp)
     const int nk = __builtin_popcount(zmask) * ncs;
 
     // ---- per-lane load offsets, fixed for the whole kernel -----------------
-    // patch slot s = (wave + NW*t)*64 + lane: chunk plane s / NPIX, patch
-    // pixel s % NPIX; weight slot s: (chunk plane, tap, channel) with the
-    // channel fastest.
+    // patch slot s = (wave + NW*t)*64 + lane: pixel-major, row s / ROWSLOTS
+    // and within it pixel-then-chunk (a row's last RSK slots and each
+    // pixel's last slot are pads that read zeros), or chunk-planar, chunk
+    // plane s / NPIX and patch pixel s % NPIX; weight slot s: (chunk plane,
+    // tap, channel) with the channel fastest.
     uint32_t pv[S::PATCH_LOADS], wv[S::W_LOADS];
 #pragma unroll
     for (int t = 0; t < S::PATCH_LOADS; ++t) {
         const int s = (wave + NW * t) * 64 + lane;
-        int q, px;
+        int q, r, c;
         if constexpr (PM) {
-            px = s / S::PPITCH;
-            q = s - px * S::PPITCH;      // q == CPL: the pad slot (zero)
+            r = s / S::ROWSLOTS;
+            const int rs = s - r * S::ROWSLOTS;
+            c = rs / S::PPITCH;
+            q = c < S::PW ? rs - c * S::PPITCH : S::CPL;   // q == CPL: a pad slot (zero)
         } else {
             q = s / S::NPIX;
-            px = s - q * S::NPIX;
+            const int px = s - q * S::NPIX;
+            r = px / S::PW;
+            c = px - r * S::PW;
         }
-        const int r = px / S::PW, c = px - r * S::PW;
         const int ih = ih0 + r, iw = iw0 + c;
         const bool ok = s < S::PSLOTS && q < S::CPL && (unsigned)ih < (unsigned)p.Hi && (unsigned)iw < (unsigned)p.Wi;
         pv[t] = ok ? (uint32_t)(((ih * p.Wi + iw) * GC + q * 8) * 2) : kOutOfRange;
@@ -213,7 +228,7 @@ patch_fixed_kernel(PatchFixedParams pp)
         int m = (wave * S::MI + i) * 32 + frow;
         m = m < S::BM ? m : 0;           // blocks past the box read pixel 0 (never stored)
         const int r = m / TW, c = m - (m / TW) * TW;
-        abase[i] = PM ? ((r * S::PW + c) * S::PPITCH + half) * 16 : half * S::PLANE + (r * S::PW + c) * 16;
+        abase[i] = PM ? (r * S::ROWSLOTS + c * S::PPITCH + half) * 16 : half * S::PLANE + (r * S::PW + c) * 16;
     }
     const int bbase = S::PATCH_BYTES + (half * S::TAPS * BN + frow) * 16;
 
@@ -243,7 +258,7 @@ patch_fixed_kernel(PatchFixedParams pp)
         auto rd = [&](int pr, int buf) __attribute__((always_inline)) {
             const int tap = pr / S::HS, h = pr - tap * S::HS;
             const int y = tap / FX, x = tap - y * FX;
-            const int aoff = PM ? ((y * DH * S::PW + x * DW) * S::PPITCH + 2 * h) * 16
+            const int aoff = PM ? (y * DH * S::ROWSLOTS + x * DW * S::PPITCH + 2 * h) * 16
                                 : 2 * h * S::PLANE + (y * DH * S::PW + x * DW) * 16;
             const int boff = ((2 * h * S::TAPS + tap) * BN) * 16;
 #pragma unroll
