@@ -139,6 +139,21 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
     const int PX = 2 * C1;                // bytes per patch row
     const int S1p = S::s1p(C1);           // conv1 reduction steps, padded to whole groups
 
+    // Biases (both convs, 2K values, three per thread) are fetched first:
+    // loads complete in issue order, so the wait for the input patch below
+    // then covers them too, and the weight ring's loads issued after the
+    // patch stay in flight across that wait.
+    constexpr int BPT = (2 * K + 255) / 256;      // bias values per thread
+    uint16_t braw[BPT];
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = tid + 256 * u;
+            const uint16_t *b = reinterpret_cast<const uint16_t *>(i < K ? cp.b1 : cp.b2);
+            braw[u] = i < 2 * K ? b[i < K ? i : (i < 2 * K ? i - K : 0)] : 0;
+        }
+    }
+
     // ---- input patch: XP positions x C1 channels, zeros outside the sequence
     {
         const i32x4_t xr = buffer_rsrc(cp.x, cp.x_bytes);
@@ -175,13 +190,14 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
         for (int j = 0; j < 3; ++j) ldw(d, d, j);
 
     float *bias_lds = reinterpret_cast<float *>(smem + S::BIAS0);
+    wait_vmcnt<3 * S::D1>();      // the biases and the patch (loads complete in issue order)
     if constexpr (BIAS) {
-        for (int i = tid; i < 2 * K; i += 256) {
-            const uint16_t *b = reinterpret_cast<const uint16_t *>(i < K ? cp.b1 : cp.b2);
-            bias_lds[i] = bf16_to_f32(b[i < K ? i : i - K]);
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = tid + 256 * u;
+            if (i < 2 * K) bias_lds[i] = bf16_to_f32(braw[u]);
         }
     }
-    wait_vmcnt<3 * S::D1>();      // the patch (loads complete in issue order)
     __syncthreads();              // input patch and biases in LDS
 
     // One reduction step: nine products, weight fragment j major, and one
