@@ -285,6 +285,58 @@ def test_workload_prepacked_weights(dev, wid):
         x = host(yp).astype(np.float32)
 
 
+def _split_records(limit=4):
+    """Tuning records whose prepacked-weight configuration differs from the
+    natural one (read from the compiled table), smallest first, at most one
+    per (dtype, natural kernel kind, prepacked kernel kind)."""
+    import os
+    here = os.path.join(os.path.dirname(__file__), "..", "convolution_forward_implicit_amd", "csrc", "selector_db.inc")
+    out, seen = [], set()
+    rows = []
+    for line in open(here):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        nat, pk = line.split('"')[1], line.split('"')[3]
+        if not pk or pk == nat:
+            continue
+        v = [int(t) for t in re.findall(r"-?\d+", line.split('"')[0])]
+        dt = "f32" if v[0] == 0 else "bf16"
+        p = sd.problem(v[2], v[3], v[4], v[5], v[6:9], v[9:12], v[12:15], v[15:18], v[18:21])
+        rows.append((ref.useful_flop(p), dt, bool(v[1]), p, nat, pk))
+    for flop, dt, ge, p, nat, pk in sorted(rows, key=lambda r: r[0]):
+        kind = (dt, nat.split("_")[1], pk.split("_")[1])
+        if kind in seen:
+            continue
+        seen.add(kind)
+        out.append((dt, ge, p, nat, pk))
+    return out[:limit]
+
+
+SPLIT_RECORDS = _split_records()
+
+
+@pytest.mark.parametrize("rec", SPLIT_RECORDS, ids=["%s_%s_to_%s" % (r[0], r[3], r[4]) for r in SPLIT_RECORDS])
+def test_plan_runs_its_prepacked_configuration(dev, rec):
+    """A recorded shape whose tuning record names another configuration for
+    prepacked weights: the plan's natural run uses the record's natural
+    configuration, its prepacked run the other one (conv_fwd_packed_config),
+    bit for bit the natural run of a plan forced to that configuration, and
+    both meet the per-element bound against the oracle."""
+    dt, ge, p, nat, pk = rec
+    names = {n: i for i, n in CONFIGS}
+    x, w, b = sd.random_inputs(p, dt, 41, ge)
+    yn, c = run(dev, p, dt, x, w, b, ge)
+    assert (" %s " % nat) in c.describe()
+    assert c.packed_config() == names[pk]
+    yp, _ = run_packed(dev, p, dt, x, w, b, ge)
+    yf, _ = run(dev, p, dt, x, w, b, ge, config=names[pk])
+    assert same_bits(yp, yf)
+    idx = sample_indices(p, 3000, 43) if ref.useful_flop(p) > 4e9 else None
+    assert_close(host(yn), p, dt, x, w, b, ge, idx)
+    assert_close(host(yp), p, dt, x, w, b, ge, idx)
+
+
 @pytest.mark.parametrize("name_re", [r"_dma_", r"_pfix_"])
 def test_prepacked_image_holds_every_weight_chunk(dev, name_re):
     """The packed image is a rearrangement of w with zero padding: every
