@@ -340,7 +340,9 @@ def measure(r, steps, warmup, launches, workload):
                 continue
             med = float(np.median(usp[k]))
             ach = r.flops[k] / (med * 1e-6) / 1e12
-            lay["prepacked"] = {"us_median": round(med, 3), "us_mean": round(float(np.mean(usp[k])), 3),
+            from convolution_forward_implicit_amd import capi
+            lay["prepacked"] = {"config": capi.conv_fwd_config_name(r.convs[k].packed_config()),
+                                "us_median": round(med, 3), "us_mean": round(float(np.mean(usp[k])), 3),
                                 "tflops": round(ach, 2), "frac_of_mfma_peak": round(ach / PEAK_TFLOPS[r.dt], 4),
                                 "bytes": int(r.sets[0]["wp"][k].numel())}
             if "target" in lay:
