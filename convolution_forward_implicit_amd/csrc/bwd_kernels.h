@@ -113,9 +113,10 @@ namespace convfwd {
 // goes to a caller workspace [split][g][k][t][c], and wgrad_reduce_kernel
 // sums the splits in index order (deterministic) and rounds to bf16.  The
 // 32x32x16 bf16 MFMA takes dy rows as the first operand (k) and x rows as
-// the second (c); block b = (t * KB + kb) * CB + cb goes to wave b mod 4, so
-// a wave keeps one (kb, cb) over its taps and reads its dy fragment once per
-// step.  Channels per group must be multiples of 8 (16-byte rows).
+// the second (c); block b = (t * KB + kb) * CB + cb goes to wave b mod NWV
+// (the workgroup's wave count, a multiple of KB * CB), so a wave keeps one
+// (kb, cb) over its taps and reads its dy fragment once per step.  Channels
+// per group must be multiples of 8 (16-byte rows).
 struct WgradParams {
     const void *x, *dy;
     float *ws;                 // partials [split][G][K][taps][C]
@@ -133,29 +134,30 @@ struct WgradParams {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 
-template <int KT, int CT, int TT>
+template <int KT, int CT, int TT, int NWV>
 struct WgradShape {
+    static constexpr int NT = NWV * 64;                 // threads of the workgroup
     static constexpr int PC = 32;                       // pixels per K-step
     static constexpr int QN = CT / 8;                   // 16-byte chunks per pixel row
     static constexpr int RG = TT + 1;                   // row groups: dy, then one per tap
     static constexpr int PITCH = 72;                    // bytes per LDS row
     static constexpr int ROWS = KT + TT * CT;
     static constexpr int LDS_BYTES = ROWS * PITCH;
-    static constexpr int NTG = 256 / (QN * PC / 2);     // thread groups over the row groups
+    static constexpr int NTG = NT / (QN * PC / 2);      // thread groups over the row groups
     static constexpr int UPT = (RG + NTG - 1) / NTG;    // staging units per thread
     static constexpr int KB = KT / 32, CB = CT / 32;
     static constexpr int NBLK = TT * KB * CB;           // 32x32 output blocks
-    static constexpr int NBW = (NBLK + 3) / 4;          // blocks per wave
+    static constexpr int NBW = (NBLK + NWV - 1) / NWV;  // blocks per wave
     static_assert(KT == CT, "one chunk count for both operands");
     static_assert(KT == 32 || KT == 64, "32 or 64 channels per tile");
     static_assert(NBW * 16 <= 160, "accumulators");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
-template <int KT, int CT, int TT>
-__global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
+template <int KT, int CT, int TT, int NWV>
+__global__ void __launch_bounds__(NWV * 64) wgrad_kernel(WgradParams wp)
 {
-    using S = WgradShape<KT, CT, TT>;
+    using S = WgradShape<KT, CT, TT, NWV>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -296,7 +298,7 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
 
     // Fragments are read as 32-bit words and reinterpreted as bf16 at the
     // product (as bf16 vectors the compiler repacks them element by element).
-    // Every wave runs NBW blocks: a block past the last (when 4 does not
+    // Every wave runs NBW blocks: a block past the last (when NWV does not
     // divide the count) reads the last block's rows and its sums are never
     // stored, so no read or product is predicated.
     constexpr int NM = 2 * S::NBW;              // products per wave and step
@@ -319,11 +321,11 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
             const int co = 32 * s + 16 * kh;  // byte offset of the lane's 8 pixels
 #pragma unroll
             for (int i = 0; i < S::NBW; ++i) {
-                // block wave + 4i: with 2x2 channel blocks the wave keeps its
-                // (kb, cb) and i is the tap; with one channel block the block is the tap
-                int t, kb, cb;
-                if (S::CB * S::KB == 4) { t = i; kb = wave >> 1; cb = wave & 1; }
-                else { t = min(wave + 4 * i, S::NBLK - 1); kb = 0; cb = 0; }
+                // block wave + NWV i (a block past the last reads the last
+                // one's rows): with NWV a multiple of the KB x CB channel
+                // blocks a wave keeps its (kb, cb) and i walks the taps
+                const int blk = min(wave + NWV * i, S::NBLK - 1);
+                const int t = blk / (S::KB * S::CB), kb = (blk / S::CB) % S::KB, cb = blk % S::CB;
                 // rows are 8-byte aligned (72-byte pitch): two 8-byte LDS reads per fragment
                 fa[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (kb * 32 + frow) * S::PITCH + co);
                 fb[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (KT + t * CT + cb * 32 + frow) * S::PITCH + co);
@@ -357,7 +359,7 @@ __global__ void __launch_bounds__(256) wgrad_kernel(WgradParams wp)
     float *wsg = wp.ws + ((int64_t)split * wp.G + g) * (int64_t)wp.K * wp.taps * wp.C;
 #pragma unroll
     for (int i = 0; i < S::NBW; ++i) {
-        const int blk = wave + 4 * i;
+        const int blk = wave + NWV * i;
         if (blk < S::NBLK) {
             const int cb = blk % S::CB, kb = (blk / S::CB) % S::KB, t = t0 + blk / (S::CB * S::KB);
             const int c = c0 + cb * 32 + frow;

@@ -136,19 +136,20 @@ void launch_patchf(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStr
         hipExtLaunchKernelGGL((patch_fixed_kernel<TH, TW, BN, CC, NS, FY, FX, DH, DW, NW, PM, RA, RR, false, false>), g, b, 0, s, e0, e1, 0, pp);
 }
 
-template <int KT, int TT>
+template <int KT, int TT, int NWV>
 void launch_wgrad(const WgradParams &wp, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((wgrad_kernel<KT, KT, TT>), dim3(grid), dim3(256), 0, s, wp);
+    hipLaunchKernelGGL((wgrad_kernel<KT, KT, TT, NWV>), dim3(grid), dim3(NWV * 64), 0, s, wp);
 }
 
 // Workgroups of one backward-weight instantiation that a compute unit holds
 // at once (its registers and LDS decide); 1 when the runtime cannot tell.
-template <int KT, int TT>
+template <int KT, int TT, int NWV>
 int wgrad_occupancy()
 {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, wgrad_kernel<KT, KT, TT>, 256, 0) != hipSuccess) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, wgrad_kernel<KT, KT, TT, NWV>, NWV * 64, 0) !=
+        hipSuccess) {
         (void)hipGetLastError();
         return 1;
     }
@@ -468,6 +469,7 @@ struct conv_bwd_weight_plan {
     conv_fwd_desc_t desc;     // the forward problem
     WgradParams wp;           // pointers filled per run
     int KT, TT;               // tile: KT x KT channels, TT taps
+    int NWV;                  // waves per workgroup
     int occ;                  // workgroups per CU at once
     int grid;
     int64_t x_elems, dy_elems, dw_elems, ws_bytes;
@@ -1397,11 +1399,23 @@ conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weigh
     // partial tile that the reduction reads back, so more splits than the
     // CUs can run at once only add traffic (at 112 splits of the grouped 2-D
     // workload the reduction took a third of the time).
+    // Eight waves for the tiles with many 32x32 output blocks (64 channels x
+    // 9 taps: 36, 32 x 27: 27): two waves per SIMD overlap each other's
+    // staging and products (grouped 2-D workload +11%, 3-D +3%, same box);
+    // with fewer blocks (64 x 3 taps: 12) a quarter of eight waves' block
+    // slots would idle and four waves are faster (batch-32 frontend: 271 vs
+    // 237 TFLOP/s).
+    const bool eight = (pl->KT == 64 && pl->TT == 9) || (pl->KT == 32 && pl->TT == 27);
+    pl->NWV = eight ? 8 : 4;
     int occ = 1;
-    if (pl->KT == 64) occ = pl->TT == 9 ? wgrad_occupancy<64, 9>() : pl->TT == 3 ? wgrad_occupancy<64, 3>()
-                                                                                   : wgrad_occupancy<64, 1>();
-    else occ = pl->TT == 27 ? wgrad_occupancy<32, 27>() : pl->TT == 9 ? wgrad_occupancy<32, 9>()
-                            : pl->TT == 3 ? wgrad_occupancy<32, 3>() : wgrad_occupancy<32, 1>();
+    if (eight) {
+        occ = pl->KT == 64 ? wgrad_occupancy<64, 9, 8>() : wgrad_occupancy<32, 27, 8>();
+    } else {
+        if (pl->KT == 64) occ = pl->TT == 9 ? wgrad_occupancy<64, 9, 4>() : pl->TT == 3 ? wgrad_occupancy<64, 3, 4>()
+                                                                                         : wgrad_occupancy<64, 1, 4>();
+        else occ = pl->TT == 27 ? wgrad_occupancy<32, 27, 4>() : pl->TT == 9 ? wgrad_occupancy<32, 9, 4>()
+                                : pl->TT == 3 ? wgrad_occupancy<32, 3, 4>() : wgrad_occupancy<32, 1, 4>();
+    }
     pl->occ = occ;
     int64_t splits = std::max<int64_t>(1, (int64_t)device_cu_count() * occ / tiles);
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, steps / 8));
@@ -1422,9 +1436,9 @@ conv_status_t conv_bwd_weight_create(const conv_fwd_desc_t *desc, conv_bwd_weigh
     pl->grid = (int)grid;
     pl->ws_bytes = pl->dw_elems * splits * 4;
     snprintf(pl->text, sizeof(pl->text),
-             "bwd_weight bf16 tile %dx%d ch x %d taps, %lld tiles x %d splits of %d x 32 pixels, grid=%d "
-             "(%d per CU) lds=%dB",
-             pl->KT, pl->KT, pl->TT, (long long)tiles, wp.splits, wp.steps_per_split, pl->grid, pl->occ,
+             "bwd_weight bf16 tile %dx%d ch x %d taps, %d waves, %lld tiles x %d splits of %d x 32 pixels, "
+             "grid=%d (%d per CU) lds=%dB",
+             pl->KT, pl->KT, pl->TT, pl->NWV, (long long)tiles, wp.splits, wp.steps_per_split, pl->grid, pl->occ,
              pl->KT == 64 ? (64 + pl->TT * 64) * 72 : (32 + pl->TT * 32) * 72);
     if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
     *plan = pl;
@@ -1468,15 +1482,18 @@ conv_status_t conv_bwd_weight_run(const conv_bwd_weight_plan_t *plan, const void
     // skipped and the reduction over zero splits writes dw = 0.
     const bool empty = plan->dy_elems == 0;
     if (empty) {
+    } else if (plan->NWV == 8) {
+        if (plan->KT == 64) launch_wgrad<64, 9, 8>(wp, plan->grid, s);
+        else launch_wgrad<32, 27, 8>(wp, plan->grid, s);
     } else if (plan->KT == 64) {
-        if (plan->TT == 9) launch_wgrad<64, 9>(wp, plan->grid, s);
-        else if (plan->TT == 3) launch_wgrad<64, 3>(wp, plan->grid, s);
-        else launch_wgrad<64, 1>(wp, plan->grid, s);
+        if (plan->TT == 9) launch_wgrad<64, 9, 4>(wp, plan->grid, s);
+        else if (plan->TT == 3) launch_wgrad<64, 3, 4>(wp, plan->grid, s);
+        else launch_wgrad<64, 1, 4>(wp, plan->grid, s);
     } else {
-        if (plan->TT == 27) launch_wgrad<32, 27>(wp, plan->grid, s);
-        else if (plan->TT == 9) launch_wgrad<32, 9>(wp, plan->grid, s);
-        else if (plan->TT == 3) launch_wgrad<32, 3>(wp, plan->grid, s);
-        else launch_wgrad<32, 1>(wp, plan->grid, s);
+        if (plan->TT == 27) launch_wgrad<32, 27, 4>(wp, plan->grid, s);
+        else if (plan->TT == 9) launch_wgrad<32, 9, 4>(wp, plan->grid, s);
+        else if (plan->TT == 3) launch_wgrad<32, 3, 4>(wp, plan->grid, s);
+        else launch_wgrad<32, 1, 4>(wp, plan->grid, s);
     }
     const int64_t n = plan->dw_elems;   // a multiple of 8 (C % 8 == 0)
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((unsigned)((n / 4 + 63) / 64)), dim3(64), 0, s,
