@@ -435,6 +435,48 @@ def test_edge_cases(dev, name, p, dt):
         assert np.array_equal(bits(y), check.round_to_bf16_bits(r))
 
 
+def _random_problems(n=48, seed=2026):
+    """Seeded random problems the calibration sweep never saw: 1-D / 2-D /
+    3-D, groups, strides, padding, dilation, ragged channel counts, both
+    dtypes, with and without bias + GELU; small enough for the oracle."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < n:
+        nd = int(rng.integers(1, 4))
+        dt = "bf16" if rng.random() < 0.6 else "f32"
+        G = int(rng.choice([1, 1, 2, 4, 8]))
+        C = int(rng.choice([8, 16, 24, 32, 40, 64, 80, 96, 3, 13]))
+        K = int(rng.choice([8, 16, 32, 48, 64, 72, 96, 128, 5, 19]))
+        ins, filt, st, pad, dil = [1, 1, 1], [1, 1, 1], [1, 1, 1], [0, 0, 0], [1, 1, 1]
+        for d in range(3 - nd, 3):
+            ins[d] = int(rng.integers(4, 40 if nd == 3 else (64 if nd == 2 else 900)))
+            filt[d] = int(rng.choice([1, 3, 3, 5]))
+            st[d] = int(rng.choice([1, 1, 2, 3]))
+            pad[d] = int(rng.integers(0, 3))
+            dil[d] = int(rng.choice([1, 1, 2]))
+        N = int(rng.integers(1, 4))
+        p = sd.problem(N, G, C, K, ins, filt, st, pad, dil)
+        o = ref.out_dims(p)
+        if min(o) < 1 or ref.useful_flop(p) > 6e8:
+            continue
+        ge = bool(rng.random() < 0.5)
+        out.append((dt, ge, p))
+    return out
+
+
+RANDOM_PROBLEMS = _random_problems()
+
+
+@pytest.mark.parametrize("dt,ge,p", RANDOM_PROBLEMS, ids=["r%02d_%s" % (i, r[0]) for i, r in enumerate(RANDOM_PROBLEMS)])
+def test_selector_on_random_shapes(dev, dt, ge, p):
+    """Whatever configuration the selector (cost model or record) picks for a
+    shape outside the calibration grid, every output meets the per-element
+    bound against the oracle."""
+    x, w, b = sd.random_inputs(p, dt, 47, ge)
+    y, c = run(dev, p, dt, x, w, b, ge)
+    assert_close(host(y), p, dt, x, w, b, ge)
+
+
 def test_input_of_2gib_and_more_bit_exact(dev):
     """An input of 2 GiB or more (bf16 [16, 1048600, 64], 2.00005 GiB): the
     direct-to-LDS kernels address x with 32-bit byte offsets and are not
