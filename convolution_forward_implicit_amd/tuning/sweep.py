@@ -1,7 +1,7 @@
 """Times every eligible tile configuration on a grid of convolution problems
 through the C ABI and writes one CSV row per (problem, configuration).
 
-    python -m convolution_forward_implicit_amd.tuning.sweep OUT.csv
+    python -m convolution_forward_implicit_amd.tuning.sweep OUT.csv [PASSES]
 
 Needs a GPU.  Every problem is timed with the two epilogues the workloads
 use: none, and bias + GELU (the erf-GELU costs VALU time per output, which
@@ -10,8 +10,8 @@ caches as in the benchmark (consecutive launches rotate through copies of
 x, w, bias and y that together exceed the 256 MB last-level cache), 40
 launches to raise the clock, then per configuration 3 untimed launches and
 the median of 21, each timed by HIP events that the launch records when the
-kernel starts and ends; all configurations are timed twice, in opposite
-orders, and the lower median is kept.  A configuration with a
+kernel starts and ends; all configurations are timed PASSES times (default
+2), alternating between opposite orders, and the lowest median is kept.  A configuration with a
 prepacked-weight form is timed the same way from its prepacked weights too
 ("ms_packed"; empty for the others).  Inputs are random (values do not
 affect the timing).
@@ -63,7 +63,7 @@ def grid():
     return out
 
 
-def main(path):
+def main(path, passes=2):
     import torch
     from convolution_forward_implicit_amd import ConvFwd, ConvError, capi
     dev = torch.device("cuda:0")
@@ -114,9 +114,9 @@ def main(path):
                 x, w, b, y = nxt()
                 ref(x, w, b, out=y)
             best = {}
-            # two passes in opposite orders, the lower median kept: a clock that
+            # passes in alternating opposite orders, the lowest median kept: a clock that
             # is still rising favours no particular position in the table
-            for order in (plans, plans[::-1]):
+            for order in [plans, plans[::-1]] * ((passes + 1) // 2):
                 for name, c, run in order:
                     for _ in range(3):
                         run()
@@ -145,4 +145,4 @@ def main(path):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1] if len(sys.argv) > 1 else "sweep.csv")
+    main(sys.argv[1] if len(sys.argv) > 1 else "sweep.csv", int(sys.argv[2]) if len(sys.argv) > 2 else 2)
