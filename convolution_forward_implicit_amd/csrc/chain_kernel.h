@@ -316,8 +316,7 @@ __global__ void __launch_bounds__(256) chain_kernel(ChainParams cp)
         const int row = idx / VPR, v = idx - row * VPR;
         const int o = o0 + row;
         if (o >= cp.Lo) continue;
-        *reinterpret_cast<uint4 *>(yg + ((size_t)n * cp.Lo + o) * K + v * 8) =
-            *reinterpret_cast<const uint4 *>(Ys + row * S::YP + v * 16);
+        store_nt16(yg + ((size_t)n * cp.Lo + o) * K + v * 8, *reinterpret_cast<const uint4 *>(Ys + row * S::YP + v * 16));
     }
 }
 

@@ -371,8 +371,8 @@ __global__ void __launch_bounds__(256, 1) chain_packed_kernel(ChainPackedParams 
     const int rows = cp.Lo - o0 < S::TO ? cp.Lo - o0 : S::TO;
     for (int idx = tid; idx < rows * VPR; idx += 256) {
         const int row = idx / VPR, v = idx - row * VPR;
-        *reinterpret_cast<uint4 *>(yg + ((size_t)n * cp.Lo + o0 + row) * K + v * 8) =
-            *reinterpret_cast<const uint4 *>(Ys + row * S::YP + v * 16);
+        store_nt16(yg + ((size_t)n * cp.Lo + o0 + row) * K + v * 8,
+                   *reinterpret_cast<const uint4 *>(Ys + row * S::YP + v * 16));
     }
 }
 

@@ -639,15 +639,18 @@ igemm_dma_kernel(DmaParams dp)
                 pk.z = f32x2_to_bf16x2(v[it][4], v[it][5]);
                 pk.w = f32x2_to_bf16x2(v[it][6], v[it][7]);
                 if (p.out_vec) {
-                    *reinterpret_cast<uint4 *>(dst) = pk;
-                } else {
-                    const uint16_t *hv = reinterpret_cast<const uint16_t *>(&pk);
+                    store_nt16(dst, pk);
+                } else {   // the halfwords taken from the packed words (no type punning)
                     const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
-                    for (int e = 0; e < lim; ++e) dst[e] = hv[e];
+                    const uint32_t wd[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+                    for (int e = 0; e < S::VEC; ++e)
+                        if (e < lim) dst[e] = (uint16_t)(wd[e >> 1] >> ((e & 1) * 16));
                 }
             } else {
                 if (p.out_vec) {
-                    *reinterpret_cast<f32x4_t *>(dst) = f32x4_t{v[it][0], v[it][1], v[it][2], v[it][3]};
+                    __builtin_nontemporal_store(f32x4_t{v[it][0], v[it][1], v[it][2], v[it][3]},
+                                                reinterpret_cast<f32x4_t *>(dst));
                 } else {
                     const int lim = (p.K - n) < S::VEC ? (p.K - n) : S::VEC;
                     for (int e = 0; e < lim; ++e) dst[e] = v[it][e];
@@ -759,7 +762,7 @@ igemm_dma_kernel(DmaParams dp)
             const int m = m0 + row_of[it];
             const int n = n0 + (idx % OVPR) * S::VEC;
             if (idx < NVP && m < p.M && n < p.K)
-                *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
+                __builtin_nontemporal_store(val[it], reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n));
         }
     }
 }

@@ -438,7 +438,7 @@ patch_fixed_kernel(PatchFixedParams pp)
         const int n = n0 + (idx % OVPR) * 8;
         if (idx < NV && oh < p.Ho && ow < p.Wo && n < p.K) {
             const int m = ((nimg * p.Do + od) * p.Ho + oh) * p.Wo + ow;
-            *reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n) = val[it];
+            __builtin_nontemporal_store(val[it], reinterpret_cast<i32x4_t *>(yg + (size_t)m * GK + n));
         }
     }
 }
