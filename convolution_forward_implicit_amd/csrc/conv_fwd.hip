@@ -322,6 +322,8 @@ const TileCfg kCfgs[] = {
     DMA2(0, 64, 64, 2, 2, 2, 16, 1),
     DMA4(0, 48, 48, 2, 16, 1),
     DMA4F(0, 48, 48, 2, 16, 1, 4),
+    DMAX(0, 48, 48, 1, 3, 3, 16, 1, 4, 4, "f32_dma_48x48_w1x3_s3_m16_k1_g4_f4"),
+    DMAX(0, 48, 48, 3, 1, 3, 16, 1, 4, 4, "f32_dma_48x48_w3x1_s3_m16_k1_g4_f4"),
     DMAX(0, 48, 48, 3, 1, 2, 16, 1, 4, 4, "f32_dma_48x48_w3x1_s2_m16_k1_g4_f4"),
     DMAX(0, 48, 48, 1, 3, 2, 16, 1, 4, 4, "f32_dma_48x48_w1x3_s2_m16_k1_g4_f4"),
     DMAX(0, 48, 96, 3, 2, 2, 16, 2, 2, 0, "f32_dma_48x96_w3x2_s2_m16_k2_g2"),
