@@ -1,8 +1,9 @@
-"""The forward entry points under HIP graph capture.
+"""The library's entry points under HIP graph capture.
 
-conv_fwd_run, conv_fwd_run_packed and conv_chain_run_packed allocate
-nothing and enqueue only kernels on the caller's stream, so a caller can
-capture them in a HIP graph and replay it.  Each graph is captured once,
+conv_fwd_run, conv_fwd_run_packed, conv_chain_run_packed and the backward
+passes (with a caller workspace) allocate nothing and enqueue only kernels
+on the caller's stream, so a caller can capture them in a HIP graph and
+replay it.  Each graph is captured once,
 then replayed several times with other eager work of the library between
 the replays; every replay's output is compared bit for bit with the eager
 run of the same inputs (the eager path itself is checked against the
@@ -102,3 +103,56 @@ def test_chain_graph_replays_match_eager(dev):
                           lambda: ch.run_packed(x2, wp, b1, b2, out=y2))
     for k, o in enumerate(outs):
         assert torch.equal(o.view(torch.int16), y_eager.view(torch.int16)), k
+
+
+BWD_DATA_CASES = {
+    "strided_1d_bf16": (sd.conv1d_problem(4, 96, 64, 600, 3, 2, 1), "bf16"),       # spread dy
+    "unit_2d_f32": (sd.problem(2, 2, 16, 24, (1, 20, 18), (1, 3, 3), (1, 1, 1), (0, 1, 1)), "f32"),
+    "dilated_3d_bf16": (sd.problem(1, 4, 32, 32, (6, 14, 14), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2)), "bf16"),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BWD_DATA_CASES))
+def test_bwd_data_graph_replays_match_eager(dev, case):
+    """Backward-data (weight flip, dy spread where strided, the forward
+    kernels) captured with a caller workspace."""
+    from convolution_forward_implicit_amd import ConvBwdData
+    p, dt = BWD_DATA_CASES[case]
+    bd = ConvBwdData(p, dt)
+    print("case: graph bwd_data", case, bd.describe(), flush=True)
+    rng = np.random.Generator(np.random.PCG64(7))
+    dy = _up(rng.uniform(-1, 1, bd.dy_shape), dt, dev)
+    w = _up(rng.normal(0, 0.05, bd.w_shape), dt, dev)
+    ws = torch.empty(max(bd.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    dx_eager = bd(dy, w, workspace=ws)
+    torch.cuda.synchronize()
+    dx = torch.empty_like(dx_eager)
+    dy2 = _up(rng.uniform(-1, 1, bd.dy_shape), dt, dev)
+    dx2 = torch.empty_like(dx_eager)
+    outs = _replays_match(dev, lambda s: bd(dy, w, out=dx, stream=s, workspace=ws), dx,
+                          lambda: bd(dy2, w, out=dx2, workspace=ws))
+    view = torch.int16 if dt == "bf16" else torch.int32
+    for k, o in enumerate(outs):
+        assert torch.equal(o.view(view), dx_eager.view(view)), k
+
+
+def test_bwd_weight_graph_replays_match_eager(dev):
+    """Backward-weight (split partials in the workspace, then their ordered
+    sum) captured with a caller workspace."""
+    from convolution_forward_implicit_amd import ConvBwdWeight
+    p = sd.problem(4, 4, 64, 64, (1, 28, 28), (1, 3, 3), (1, 1, 1), (0, 1, 1))
+    bw = ConvBwdWeight(p)
+    print("case: graph bwd_weight", bw.describe(), flush=True)
+    rng = np.random.Generator(np.random.PCG64(8))
+    x = _up(rng.uniform(-1, 1, bw.x_shape), "bf16", dev)
+    dy = _up(rng.uniform(-1, 1, bw.dy_shape), "bf16", dev)
+    ws = torch.empty(max(bw.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    dw_eager = bw(x, dy, workspace=ws)
+    torch.cuda.synchronize()
+    dw = torch.empty_like(dw_eager)
+    dy2 = _up(rng.uniform(-1, 1, bw.dy_shape), "bf16", dev)
+    dw2 = torch.empty_like(dw_eager)
+    outs = _replays_match(dev, lambda s: bw(x, dy, out=dw, stream=s, workspace=ws), dw,
+                          lambda: bw(x, dy2, out=dw2, workspace=ws))
+    for k, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), dw_eager.view(torch.int16)), k
