@@ -941,3 +941,34 @@ def test_bwd_weight_empty_batch_is_zero_and_repeatable(dev):
     a, _ = run_bwd_weight(dev, q, x, dy)
     b, _ = run_bwd_weight(dev, q, x, dy)
     assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Random shapes through both backward passes (another seed than the forward
+# selector's): dx in the problem's dtype, and dw (bf16) where the
+# backward-weight kernels take the shape (C and K per group multiples of 8).
+RANDOM_BWD = _random_problems(n=32, seed=3031)
+
+
+@pytest.mark.parametrize("k,dt,p", [(i, r[0], r[2]) for i, r in enumerate(RANDOM_BWD)],
+                         ids=["b%02d_%s" % (i, r[0]) for i, r in enumerate(RANDOM_BWD)])
+def test_backward_passes_on_random_shapes(dev, k, dt, p):
+    from convolution_forward_implicit_amd import ConvBwdWeight, ConvError
+    _, w, _ = sd.random_inputs(p, dt, 1300 + k, False)
+    dy = _dy(p, dt, 1400 + k, "float")
+    dx, _ = run_bwd_data(dev, p, dt, dy, w)
+    r, a = ref.conv_bwd_data(p, dy, w)
+    st = check.check(host(dx), r, a, _terms(p["K"] * np.prod(p["filt"])), dt, False, False)
+    print("parity dx:", {q: st[q] for q in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
+    try:
+        ConvBwdWeight(p).close()
+    except ConvError:
+        return
+    x, _, _ = sd.random_inputs(p, "bf16", 1500 + k, False)
+    dy = _dy(p, "bf16", 1600 + k, "float")
+    dw, _ = run_bwd_weight(dev, p, x, dy)
+    r, a = ref.conv_bwd_weight(p, x, dy)
+    st = check.check(host(dw), r, a, _terms(_pixels(p)), "bf16", False, False)
+    print("parity dw:", {q: st[q] for q in ("ok", "n", "n_fail", "max_ratio", "cosine")}, flush=True)
+    assert st["ok"], st
