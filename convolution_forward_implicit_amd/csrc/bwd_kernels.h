@@ -295,11 +295,14 @@ __global__ void __launch_bounds__(NWV * 64) wgrad_kernel(WgradParams wp)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
     const int frow = lane & 31, kh = lane >> 5;
+    static_assert(NWV % (S::KB * S::CB) == 0, "a wave keeps one (kb, cb)");
+    constexpr int TSTEP = NWV / (S::KB * S::CB);   // taps between a wave's blocks
+    const int kbw = (wave / S::CB) % S::KB, cbw = wave % S::CB, tw0 = wave / (S::KB * S::CB);
 
     // Fragments are read as 32-bit words and reinterpreted as bf16 at the
     // product (as bf16 vectors the compiler repacks them element by element).
     // Every wave runs NBW blocks: a block past the last (when NWV does not
-    // divide the count) reads the last block's rows and its sums are never
+    // divide the count) reads the last tap's rows and its sums are never
     // stored, so no read or product is predicated.
     constexpr int NM = 2 * S::NBW;              // products per wave and step
     constexpr int NL = 2 * S::UPT;              // loads per thread and step
@@ -315,20 +318,20 @@ __global__ void __launch_bounds__(NWV * 64) wgrad_kernel(WgradParams wp)
         __syncthreads();                      // the previous step's fragments are read
         store(bsel);
         __syncthreads();                      // this step is in LDS
-        u32x4_t fa[2][S::NBW], fb[2][S::NBW];
+        // Block wave + NWV i has tap t = tw0 + TSTEP i and the wave's own
+        // (kb, cb) (NWV is a multiple of the KB x CB channel blocks), so the
+        // dy fragment is read once per 16-pixel half and serves every tap of
+        // the wave; a block past the last reads the last tap's rows.
+        u32x4_t fa[2], fb[2][S::NBW];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int co = 32 * s + 16 * kh;  // byte offset of the lane's 8 pixels
+            // rows are 8-byte aligned (72-byte pitch): two 8-byte LDS reads per fragment
+            fa[s] = *reinterpret_cast<const u32x4_a8 *>(smem + (kbw * 32 + frow) * S::PITCH + co);
 #pragma unroll
             for (int i = 0; i < S::NBW; ++i) {
-                // block wave + NWV i (a block past the last reads the last
-                // one's rows): with NWV a multiple of the KB x CB channel
-                // blocks a wave keeps its (kb, cb) and i walks the taps
-                const int blk = min(wave + NWV * i, S::NBLK - 1);
-                const int t = blk / (S::KB * S::CB), kb = (blk / S::CB) % S::KB, cb = blk % S::CB;
-                // rows are 8-byte aligned (72-byte pitch): two 8-byte LDS reads per fragment
-                fa[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (kb * 32 + frow) * S::PITCH + co);
-                fb[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (KT + t * CT + cb * 32 + frow) * S::PITCH + co);
+                const int t = min(tw0 + TSTEP * i, TT - 1);
+                fb[s][i] = *reinterpret_cast<const u32x4_a8 *>(smem + (KT + t * CT + cbw * 32 + frow) * S::PITCH + co);
             }
         }
         prep(step0 + it + 2);
@@ -337,7 +340,7 @@ __global__ void __launch_bounds__(NWV * 64) wgrad_kernel(WgradParams wp)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const int s = m / S::NBW, i = m % S::NBW;
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[s][i]),
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[s]),
                                                              __builtin_bit_cast(bf16x8_t, fb[s][i]), acc[i], 0, 0, 0);
             if (m < NL) unit(bsel, m % S::UPT, m / S::UPT);
             __builtin_amdgcn_sched_barrier(0);
