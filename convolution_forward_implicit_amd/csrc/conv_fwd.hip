@@ -124,6 +124,8 @@ void launch_patchf(const KParams &kp, uint32_t xb, uint32_t wb, int grid, hipStr
     pp.fd_tw = make_fastdiv(pp.tiles_w);
     pp.fd_th = make_fastdiv(pp.tiles_h);
     pp.fd_N = make_fastdiv(kp.N);
+    pp.fd_G = make_fastdiv(kp.G);
+    pp.group_fast = kp.C * 2 < 128 ? 1 : 0;
     const dim3 g(grid), b(NW * 64);
     const bool bias = kp.bias != nullptr;
     if (bias && kp.gelu)
