@@ -15,7 +15,9 @@
 // positions: dy[o] at position o s + off, zeros elsewhere.  That is a
 // forward convolution with stride 1, no padding, the same dilation, K input
 // channels and C output channels.  With unit strides and off >= 0 the spread
-// copy is dy itself with padding off, and no copy is made.
+// copy is dy itself with padding off, and no copy is made.  A 1-D strided
+// problem runs as its stride phases instead (below): no spread copy, and
+// none of the products with its zeros.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +40,49 @@ __global__ void __launch_bounds__(256) bwd_data_weights_kernel(const T *__restri
     const int c = (int)(t % C); t /= C;
     const int64_t g = t;
     wt[i] = w[((((g * K + k) * Z + (Z - 1 - z)) * Y + (Y - 1 - y)) * X + (X - 1 - xx)) * C + c];
+}
+
+// Stride phases of a 1-D input gradient (stride s > 1 along W).  Input
+// position i = s j + f takes the taps t with (f + p - t d) divisible by s,
+// dy[j + (f + p - t d) / s]: for each phase f a stride-1 forward convolution
+// of dy itself, with those taps (largest first, so the dy offset grows by
+// d / gcd(s, d) per tap) -- no spread copy and no products with its zeros.
+// Phase f's filter is w_f[g][c][u][k] = w[g][k][tmax_f - u dt][c] (dt =
+// s / gcd(s, d)); all phases' filters are written back to back, phase f's
+// from element base[f].
+constexpr int kMaxPhases = 8;
+struct PhaseWeightParams {
+    int G, K, C, X;                   // groups, channels and taps of w
+    int nphase, dt;
+    int ntap[kMaxPhases], tmax[kMaxPhases];
+    int64_t base[kMaxPhases + 1];     // each phase's filter starts 256-byte aligned; base[nphase] = the total
+};
+
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_data_phase_weights_kernel(const T *__restrict__ w, T *__restrict__ wt,
+                                                                     PhaseWeightParams q)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // the phase of element i, and its tap count, first tap and base, by
+    // unrolled selects (a dynamic index into the argument arrays would copy
+    // them to scratch memory)
+    int f = 0;
+#pragma unroll
+    for (int r = 1; r < kMaxPhases; ++r)
+        if (r < q.nphase && i >= q.base[r]) f = r;
+    int64_t b = q.base[0];
+    int F = q.ntap[0], tm = q.tmax[0];
+#pragma unroll
+    for (int r = 1; r < kMaxPhases; ++r)
+        if (r == f) { b = q.base[r]; F = q.ntap[r]; tm = q.tmax[r]; }
+    // the alignment gap after a phase's filter, and past the last one
+    if (i - b >= (int64_t)q.G * q.C * F * q.K) return;
+    int64_t t = i - b;
+    const int k = (int)(t % q.K); t /= q.K;
+    const int u = (int)(t % F); t /= F;
+    const int c = (int)(t % q.C); t /= q.C;
+    const int64_t g = t;
+    wt[i] = w[((g * q.K + k) * q.X + (tm - u * q.dt)) * q.C + c];
 }
 
 struct SpreadParams {

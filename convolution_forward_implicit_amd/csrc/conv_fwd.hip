@@ -461,12 +461,17 @@ struct conv_chain_plan {
 
 struct conv_bwd_data_plan {
     conv_fwd_desc_t desc;     // the forward problem
-    conv_fwd_plan_t *fwd;     // dx = forward conv of (dyp or dy) with w'
+    conv_fwd_plan_t *fwd;     // dx = forward conv of (dyp or dy) with w' (no stride phases)
     bool spread;              // build the zero-inserted copy of dy
     SpreadParams sp;          // pointers filled per run
+    // > 0: a 1-D strided problem run as nphase stride phases, each a forward
+    // conv of dy itself writing every s-th row of dx (no spread copy)
+    int nphase;
+    conv_fwd_plan_t *phase[kMaxPhases];
+    PhaseWeightParams pwp;    // the phases' filters, at pwp.base[f] elements into the workspace
     int64_t dy_elems, w_elems, dx_elems;
     int64_t ws_wt, ws_dyp, ws_bytes;   // workspace: w' at 0, dyp at ws_wt
-    char text[400];
+    char text[1200];
 };
 
 struct conv_bwd_weight_plan {
@@ -778,6 +783,7 @@ static conv_status_t create_impl(const conv_fwd_desc_t *desc, int32_t forced, co
     kp.fd_Y = make_fastdiv(kp.Y);
     kp.fd_tn = make_fastdiv(kp.tiles_n);
     kp.fd_tm = make_fastdiv(kp.tiles_m);
+    kp.ldy = (int)(d.G * d.K);
     // prepacked weight image of this plan's kernel (none for the register-staged one)
     PackParams &pk = pl->pk;
     pk.esz = pl->esz;
@@ -1199,6 +1205,85 @@ conv_status_t conv_chain_useful_flop(const conv_chain_plan_t *plan, int64_t *flo
 void conv_chain_destroy(conv_chain_plan_t *plan) { delete plan; }
 
 // ---- Backward-data ---------------------------------------------------------
+// The stride phases of a 1-D strided input gradient (see bwd_kernels.h):
+// builds pl->phase[] and pl->pwp and returns true, or returns false (and
+// leaves nothing allocated) where the rewrite does not apply: more than one
+// spatial dimension, a stride beyond kMaxPhases, a phase without taps, rows
+// of dx that a fixed pitch cannot address (N > 1 with the length not a
+// multiple of the stride), a group row of dx that is not a whole number of
+// 16-byte vectors, or a phase convolution a plan cannot be made for.
+static bool make_phases(const conv_fwd_desc_t &d, const int64_t o[3], conv_bwd_data_plan *pl)
+{
+    const int64_t esz = d.dtype == CONV_DT_BF16 ? 2 : 4;
+    const int64_t s = d.stride[2], F = d.filt[2], dl = d.dilation[2], p = d.pad[2], L = d.in[2], Lo = o[2];
+    if (d.in[0] != 1 || d.in[1] != 1 || d.filt[0] != 1 || d.filt[1] != 1 || d.stride[0] != 1 || d.stride[1] != 1 ||
+        d.pad[0] != 0 || d.pad[1] != 0 || s < 2 || s > kMaxPhases || L < s)
+        return false;
+    if (d.N != 1 && L % s != 0) return false;
+    if ((d.G * d.C * esz) % 16 != 0) return false;
+    int64_t g = s, b = dl;
+    while (b) { const int64_t r = g % b; g = b; b = r; }
+    const int64_t dt = s / g, dp = dl / g;
+    PhaseWeightParams &q = pl->pwp;
+    q.G = (int)d.G; q.K = (int)d.K; q.C = (int)d.C; q.X = (int)F;
+    q.nphase = (int)s; q.dt = (int)dt;
+    int64_t base = 0;
+    conv_fwd_plan_t *ph[kMaxPhases] = {};
+    auto drop = [&]() {
+        for (int f = 0; f < kMaxPhases; ++f) conv_fwd_destroy(ph[f]);
+        g_err[0] = 0;   // a phase that could not be planned is not the caller's error
+        return false;
+    };
+    for (int f = 0; f < s; ++f) {
+        int64_t tmax = -1;
+        for (int64_t t = F - 1; t >= 0 && tmax < 0; --t)
+            if (((f + p - t * dl) % s + s) % s == 0) tmax = t;
+        if (tmax < 0) return drop();
+        const int64_t ntap = tmax / dt + 1;
+        const int64_t e0 = (f + p - tmax * dl) / s;   // dy offset of the first (largest) tap; exact
+        const int64_t J = (L - f + s - 1) / s;          // dx positions s j + f < L
+        conv_fwd_desc_t fd = d;                          // dx_f = conv(dy, w_f): K input, C output channels
+        fd.C = d.K;
+        fd.K = d.C;
+        fd.in[2] = Lo;
+        fd.filt[2] = ntap;
+        fd.stride[2] = 1;
+        fd.pad[2] = 0;
+        fd.dilation[2] = dp;
+        fd.has_bias = 0;
+        fd.gelu = 0;
+        if (create_impl(&fd, -1, &ph[f]) != CONV_OK) return drop();
+        conv_fwd_plan *pp = ph[f];
+        // output row j reads dy[j + e0 + u dp]: left pad -e0 (may be
+        // negative), J rows, each pitch s G C elements from the last
+        KParams &kp = pp->kp;
+        const TileCfg &c = kCfgs[pp->cfg];
+        kp.pw = (int)(-e0);
+        kp.Wo = (int)J;
+        kp.M = (int)(d.N * J);
+        kp.tiles_m = (kp.M + c.BM - 1) / c.BM;
+        kp.fd_Wo = make_fastdiv(kp.Wo);
+        kp.fd_tm = make_fastdiv(kp.tiles_m);
+        kp.ldy = (int)(s * d.G * d.C);
+        pp->out[2] = J;
+        pp->y_elems = (d.N * L - f) * d.G * d.C;   // the span from the phase's first row to the end of dx
+        pp->grid = (int)tiles_of(c, fd, pp->out);
+        delete pp->packed_plan;                    // the phases run from the natural layout
+        pp->packed_plan = nullptr;
+        const size_t n = strlen(pp->text);
+        snprintf(pp->text + n, sizeof(pp->text) - n, " [phase %d: taps %lld, dy offset %lld, %lld rows]", f,
+                 (long long)ntap, (long long)e0, (long long)J);
+        q.ntap[f] = (int)ntap;
+        q.tmax[f] = (int)tmax;
+        q.base[f] = base;
+        base += ((d.G * d.C * ntap * d.K * esz + 255) / 256 * 256) / esz;
+    }
+    q.base[s] = base;
+    for (int f = 0; f < kMaxPhases; ++f) pl->phase[f] = ph[f];
+    pl->nphase = (int)s;
+    return true;
+}
+
 conv_status_t conv_bwd_data_create(const conv_fwd_desc_t *desc, conv_bwd_data_plan_t **plan)
 {
     if (!plan) return fail(CONV_ERR_INVALID_ARG, "plan is NULL");
@@ -1221,6 +1306,23 @@ conv_status_t conv_bwd_data_create(const conv_fwd_desc_t *desc, conv_bwd_data_pl
         unit = unit && d.stride[i] == 1 && off[i] >= 0;
     }
     pl->spread = !unit;
+    if (!unit && make_phases(d, o, pl)) {
+        pl->spread = false;
+        pl->fwd = nullptr;
+        pl->dy_elems = d.N * o[0] * o[1] * o[2] * d.G * d.K;
+        pl->w_elems = d.G * d.K * d.filt[0] * d.filt[1] * d.filt[2] * d.C;
+        pl->dx_elems = d.N * d.in[0] * d.in[1] * d.in[2] * d.G * d.C;
+        pl->ws_wt = pl->pwp.base[pl->nphase] * esz;
+        pl->ws_dyp = 0;
+        pl->ws_bytes = pl->ws_wt;
+        int n = snprintf(pl->text, sizeof(pl->text), "bwd_data %s via %d stride phases of dy:",
+                         d.dtype == CONV_DT_BF16 ? "bf16" : "f32", pl->nphase);
+        for (int f = 0; f < pl->nphase && n < (int)sizeof(pl->text); ++f)
+            n += snprintf(pl->text + n, sizeof(pl->text) - n, " %s;", conv_fwd_describe(pl->phase[f]));
+        if (getenv("CONVFWD_LOG")) fprintf(stderr, "convfwd: %s\n", pl->text);
+        *plan = pl;
+        return CONV_OK;
+    }
     conv_fwd_desc_t f = d;   // dx = conv(dyp, w'): K input channels, C output channels
     f.C = d.K;
     f.K = d.C;
@@ -1304,6 +1406,24 @@ conv_status_t conv_bwd_data_run(const conv_bwd_data_plan_t *plan, const void *dy
     hipStream_t s = (hipStream_t)stream;
     unsigned char *ws = reinterpret_cast<unsigned char *>(workspace);
     (void)hipGetLastError();
+    if (plan->nphase > 0) {   // the phases' filters, then one forward conv of dy per phase
+        const PhaseWeightParams &q = plan->pwp;
+        const dim3 pg((unsigned)((q.base[q.nphase] + 255) / 256));
+        if (d.dtype == CONV_DT_BF16)
+            hipLaunchKernelGGL(bwd_data_phase_weights_kernel<uint16_t>, pg, dim3(256), 0, s, (const uint16_t *)w,
+                               (uint16_t *)ws, q);
+        else
+            hipLaunchKernelGGL(bwd_data_phase_weights_kernel<float>, pg, dim3(256), 0, s, (const float *)w,
+                               (float *)ws, q);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return fail(CONV_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+        for (int f = 0; f < plan->nphase; ++f) {
+            const conv_status_t st = conv_fwd_run(plan->phase[f], dy, ws + q.base[f] * esz, nullptr,
+                                                  reinterpret_cast<unsigned char *>(dx) + f * d.G * d.C * esz, stream);
+            if (st != CONV_OK) return st;
+        }
+        return CONV_OK;
+    }
     const int64_t wb = (plan->w_elems + 255) / 256;
     if (d.dtype == CONV_DT_BF16)
         hipLaunchKernelGGL(bwd_data_weights_kernel<uint16_t>, dim3((unsigned)wb), dim3(256), 0, s,
@@ -1353,6 +1473,7 @@ void conv_bwd_data_destroy(conv_bwd_data_plan_t *plan)
 {
     if (!plan) return;
     conv_fwd_destroy(plan->fwd);
+    for (int f = 0; f < kMaxPhases; ++f) conv_fwd_destroy(plan->phase[f]);
     delete plan;
 }
 

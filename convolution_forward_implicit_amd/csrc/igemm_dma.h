@@ -559,7 +559,7 @@ igemm_dma_kernel(DmaParams dp)
     __syncthreads();
 
     T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;
-    const int GK = p.G * p.K;
+    const int GK = p.ldy;   // output row pitch
     constexpr int OVPR = BN / S::VEC;
 
     // ---- split reduction: all waves share the epilogue ---------------------

@@ -81,6 +81,9 @@ struct KParams {
                         // fixed-filter patch kernels), not GKZYXC
     FastDiv fd_Wo, fd_Ho, fd_Do, fd_C, fd_X, fd_Y;
     FastDiv fd_tn, fd_tm;   // tiles_n, tiles_m
+    int ldy;            // elements from one output pixel's row to the next: G*K, or more when
+                        // the output is every s-th pixel of a larger tensor (a stride phase of
+                        // the input gradient)
 };
 
 template <int BYTES> struct RawVec;
@@ -404,7 +407,7 @@ igemm_fwd_kernel(KParams p)
     __syncthreads();
 
     T *__restrict__ yg = reinterpret_cast<T *>(p.y) + g * p.K;
-    const int GK = p.G * p.K;
+    const int GK = p.ldy;
     constexpr int OVPR = BN / S::OV;
     for (int idx = tid; idx < BM * OVPR; idx += S::NT) {
         const int row = idx / OVPR;

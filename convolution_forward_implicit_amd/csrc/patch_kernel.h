@@ -308,7 +308,7 @@ patch_conv_kernel(PatchParams pp)
     __syncthreads();
 
     uint16_t *__restrict__ yg = reinterpret_cast<uint16_t *>(p.y) + g * p.K;
-    const int GK = p.G * p.K;
+    const int GK = p.ldy;   // output row pitch
     constexpr int OVPR = BN / 8;
     if (!p.out_vec) {   // K not a whole number of vectors: element stores
         for (int idx = tid; idx < S::BM * OVPR; idx += S::NT) {

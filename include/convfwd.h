@@ -283,7 +283,13 @@ const char *conv_chain_describe(const conv_chain_plan_t *plan);
  * spread onto a grid of Di + dd(Z-1) (etc.) positions with tap-flipped,
  * channel-swapped weights, both written to a caller-owned device workspace
  * of conv_bwd_data_workspace_bytes bytes (16-byte aligned; with unit strides
- * and pad <= d(F-1) only the weights).  The library allocates nothing.
+ * and pad <= d(F-1) only the weights).  A 1-D problem with stride s > 1 runs
+ * instead as s forward convolutions of dy itself, one per stride phase (dx
+ * positions i = s j + f take the taps t with f + p - t d divisible by s),
+ * each writing every s-th row of dx, with only the phases' filters in the
+ * workspace -- where every phase has taps, N = 1 or the length is a
+ * multiple of s, and a group's row of dx is whole 16-byte vectors; the
+ * result is the same sum in another order.  The library allocates nothing.
  * Ownership, threading and asynchrony as conv_fwd; errors as conv_fwd_create
  * and conv_fwd_run, plus INVALID_ARG for a workspace that is NULL, too small
  * or overlapping dy, w or dx. */

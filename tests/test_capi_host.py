@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from convolution_forward_implicit_amd import capi, desc_from_problem, ConvFwd, ConvError
@@ -555,12 +556,21 @@ def test_bwd_data_create_workspace_and_describe():
         assert "padded dy" in capi.conv_bwd_data_describe(plan)
     finally:
         capi.conv_bwd_data_destroy(plan)
-    # stride 2: the spread copy of dy (N x (L + 2) x K) follows the weights
+    # 1-D stride 2: the stride phases' filters only (phase 0 one tap, phase 1
+    # two, each 256-byte aligned)
     p = sd.conv1d_problem(32, 384, 384, 3000, 3, 2, 1)
     plan = capi.conv_bwd_data_create(desc_from_problem(p, "f32"))
     try:
-        wt = (384 * 3 * 384 * 4 + 255) // 256 * 256
-        assert capi.conv_bwd_data_workspace_bytes(plan) == wt + 32 * 3002 * 384 * 4
+        assert capi.conv_bwd_data_workspace_bytes(plan) == 384 * 1 * 384 * 4 + 384 * 2 * 384 * 4
+        assert "2 stride phases" in capi.conv_bwd_data_describe(plan)
+    finally:
+        capi.conv_bwd_data_destroy(plan)
+    # 2-D stride 2: the spread copy of dy (N x (H + 2) x (W + 2) x K) follows the weights
+    p = sd.problem(2, 1, 16, 24, (1, 13, 11), (1, 3, 3), (1, 2, 2), (0, 1, 1))
+    plan = capi.conv_bwd_data_create(desc_from_problem(p, "f32"))
+    try:
+        wt = (24 * 9 * 16 * 4 + 255) // 256 * 256
+        assert capi.conv_bwd_data_workspace_bytes(plan) == wt + 2 * 15 * 13 * 24 * 4
         assert "spread dy" in capi.conv_bwd_data_describe(plan)
     finally:
         capi.conv_bwd_data_destroy(plan)
@@ -619,3 +629,25 @@ def test_bwd_weight_create_and_rejects():
         capi.conv_bwd_weight_create(desc_from_problem(p, "bf16", 1, 0))
     assert e.value.status == capi.CONV_ERR_UNSUPPORTED
     capi.conv_bwd_weight_destroy(None)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_data_strided_1d_runs_as_stride_phases(dtype):
+    """A 1-D strided input gradient is planned as one forward conv of dy per
+    stride phase (no spread copy) where every phase has taps, dx rows have a
+    fixed pitch (N = 1 or the length a multiple of the stride) and a group
+    row of dx is whole 16-byte vectors; otherwise dy is spread."""
+    from convolution_forward_implicit_amd import ConvBwdData
+    phases = [sd.conv1d_problem(32, 384, 384, 3000, 3, 2, 1), sd.conv1d_problem(1, 384, 384, 3000, 3, 2, 1),
+              sd.conv1d_problem(2, 16, 8, 60, 5, 3, 2), sd.conv1d_problem(1, 8, 16, 50, 7, 4, 3),
+              sd.conv1d_problem(2, 8, 8, 40, 3, 2, 1, 3)]
+    spread = [sd.conv1d_problem(2, 64, 48, 301, 3, 2, 1),            # N > 1, length not a multiple of 2
+              sd.conv1d_problem(3, 3, 5, 77, 5, 2, 2),               # 3-channel rows, and N > 1 with an odd length
+              sd.problem(2, 2, 16, 24, (1, 13, 11), (1, 3, 3), (1, 2, 2), (0, 1, 2), (1, 1, 2)),   # 2-D
+              sd.conv1d_problem(1, 8, 8, 40, 3, 2, 0, 2)]            # stride 2, dilation 2: one phase has no taps
+    for p in phases:
+        c = ConvBwdData(p, dtype)
+        assert "stride phases" in c.describe(), c.describe()
+        assert c.workspace_bytes >= 2 * int(np.prod(ref.shapes(p)[1]))
+    for p in spread:
+        assert "spread" in ConvBwdData(p, dtype).describe()

@@ -106,7 +106,8 @@ def test_chain_graph_replays_match_eager(dev):
 
 
 BWD_DATA_CASES = {
-    "strided_1d_bf16": (sd.conv1d_problem(4, 96, 64, 600, 3, 2, 1), "bf16"),       # spread dy
+    "strided_1d_bf16": (sd.conv1d_problem(4, 96, 64, 600, 3, 2, 1), "bf16"),       # stride phases of dy
+    "strided_2d_bf16": (sd.problem(2, 2, 16, 24, (1, 13, 11), (1, 3, 3), (1, 2, 2), (0, 1, 2), (1, 1, 2)), "bf16"),  # spread dy
     "unit_2d_f32": (sd.problem(2, 2, 16, 24, (1, 20, 18), (1, 3, 3), (1, 1, 1), (0, 1, 1)), "f32"),
     "dilated_3d_bf16": (sd.problem(1, 4, 32, 32, (6, 14, 14), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2)), "bf16"),
 }
@@ -114,7 +115,8 @@ BWD_DATA_CASES = {
 
 @pytest.mark.parametrize("case", sorted(BWD_DATA_CASES))
 def test_bwd_data_graph_replays_match_eager(dev, case):
-    """Backward-data (weight flip, dy spread where strided, the forward
+    """Backward-data (weight flip or the stride phases' filters, dy spread
+    for strided problems the phases do not cover, the forward
     kernels) captured with a caller workspace."""
     from convolution_forward_implicit_amd import ConvBwdData
     p, dt = BWD_DATA_CASES[case]

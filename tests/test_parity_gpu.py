@@ -744,6 +744,11 @@ BWD = [
     ("odd_channels_s2", sd.conv1d_problem(3, 3, 5, 77, 5, 2, 2)),
     ("stride_gt_filter", sd.problem(2, 1, 16, 8, (1, 17, 19), (1, 2, 2), (1, 3, 3), (0, 0, 1))),
     ("mixed_3d", sd.problem(1, 2, 5, 3, (4, 5, 7), (2, 1, 3), (2, 1, 3), (1, 0, 1), (1, 1, 1))),
+    # 1-D strided problems the plan runs as stride phases of dy (no spread copy)
+    ("phases_s3_k5", sd.conv1d_problem(2, 16, 8, 60, 5, 3, 2)),
+    ("phases_s4_k7_n1_odd", sd.conv1d_problem(1, 8, 16, 50, 7, 4, 3)),
+    ("phases_s2_dil3", sd.conv1d_problem(2, 8, 8, 40, 3, 2, 1, 3)),
+    ("phases_s3_dil2_n1", sd.conv1d_problem(1, 16, 16, 33, 4, 3, 0, 2)),
 ]
 
 

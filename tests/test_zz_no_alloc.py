@@ -57,7 +57,7 @@ def _same(a, b):
 
 def test_noalloc_matches_caller_workspace_two_calls_second_smaller():
     from convolution_forward_implicit_amd import capi
-    big = sd.conv1d_problem(8, 384, 384, 3000, 3, 2, 1)                   # strided: spread dy + weights
+    big = sd.conv1d_problem(8, 384, 384, 3000, 3, 2, 1)                   # strided: the stride phases' filters
     small = sd.problem(2, 4, 16, 8, (1, 13, 11), (1, 3, 3), (1, 1, 1), (0, 1, 1))   # stride 1: weights only
     cases = [(big, "bf16", 1), (small, "f32", 2)]
     plans = []
@@ -84,7 +84,7 @@ def test_noalloc_matches_caller_workspace_two_calls_second_smaller():
 
 def test_noalloc_refuses_a_workspace_beyond_the_array():
     from convolution_forward_implicit_amd import capi, desc_from_problem, ConvError
-    p = sd.conv1d_problem(32, 384, 384, 3000, 3, 2, 1)                  # spread dy of 73.8 MB
+    p = sd.problem(48, 1, 64, 64, (1, 112, 112), (1, 3, 3), (1, 2, 2), (0, 1, 1))   # 2-D strided: spread dy of 80 MB
     plan = capi.conv_bwd_data_create(desc_from_problem(p, "bf16"))
     try:
         assert capi.conv_bwd_data_workspace_bytes(plan) > capi.CONV_BWD_DATA_SCRATCH_BYTES
@@ -101,7 +101,7 @@ def test_noalloc_under_graph_capture():
     other inputs between the replays (the shared array is rewritten each
     time), every replay bit-identical to the eager result."""
     from convolution_forward_implicit_amd import capi
-    p = sd.conv1d_problem(4, 96, 64, 600, 3, 2, 1)       # strided: spread dy in the array
+    p = sd.conv1d_problem(4, 96, 64, 600, 3, 2, 1)       # strided: the stride phases' filters in the array
     plan, dy, w, dx_shape, tdt = _case(p, "bf16", 21)
     try:
         ref = _noalloc(plan, dy, w, dx_shape, tdt)
